@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the compensated-FP32 projection on one MI355X.
+
+A step is one pass of the whole path over the decode + FFN projection pair
+that shares one FP16 weight W [4096, 14336]:
+
+  1. decode:  y1 = x1 W,  x1 FP32 [1, 4096]      -> cfp32_linear (fused small-M kernel)
+  2. prefill: split(x2) then the dual-product GEMM with the merged epilogue,
+              x2 FP32 [8192, 4096]                -> cfp32_split + cfp32_gemm
+              (exactly the two launches cfp32_linear makes for M > 8)
+
+Inputs are seeded synthetic data (compensated_fp32_projection_amd.workloads)
+already resident in HBM.  Four copies of W (470 MB, more than the 256 MB
+Infinity Cache) are rotated step by step so that the decode kernel streams W
+from HBM.  ``value`` is whole-step throughput in FP32-equivalent TFLOP/s
+(2 M N K summed over both projections).  HIP events recorded on the launch
+stream inside the timed loop give each kernel's average duration; the MFMA
+roofline is taken for the GEMM, the dominant kernel.
+
+One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
+``headline`` (the 4096^3 GEMM and the M = 1 decode kernel measured on their
+own), ``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded
+sample of the same workload on this host).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compensated-FP32 GEMM TFLOP/s + % FP16 MFMA peak; GEMV GB/s % HBM"
+# MI355X published peaks: dense FP16 MFMA 2.5 PFLOP/s (256 CUs x 4096 FLOP/clk
+# x 2.4 GHz = 2516.6 TFLOP/s) and HBM3E 8 TB/s.
+PEAK_FP16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+K_, N_, M_DEC, M_PRE = 4096, 14336, 1, 8192
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_counters.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when there is none or the GEMM source has changed since."""
+    try:
+        text = open(COUNTER_SUMMARY).read()
+    except OSError:
+        return None
+    src = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(A1, A2, W, rows_per_thread: int):
+    """Time the CPU oracle's compensated linear (split, two FP32-accumulated
+    products, merge) on the decode row plus a slice of the prefill rows."""
+    import numpy as np
+    import oracle
+    threads = oracle.num_threads()
+    rows = max(1, rows_per_thread * threads)
+    A = np.concatenate([A1, A2[:rows]], axis=0)
+    t0 = time.perf_counter()
+    oracle.linear_cf32(A, W)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * A.shape[0] * K_ * N_
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"1 decode row + {rows} of the 8192 prefill rows, K=4096, N=14336 "
+                      f"(split + two FP32-accumulated products + merge, OpenMP over rows)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-per-thread", type=int, default=12)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compensated_fp32_projection_amd as cf
+    from compensated_fp32_projection_amd import workloads
+
+    cf.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    wl = workloads.decode_ffn_pair()
+    A1, A2, W = wl.A[0], wl.A[1], wl.W
+    Ws = [torch.from_numpy(W.view(np.int16)).to(dev)]
+    for _ in range(3):
+        Ws.append(Ws[0].clone())
+    x1 = torch.from_numpy(A1).to(dev)
+    x2 = torch.from_numpy(A2).to(dev)
+    y1 = torch.empty((M_DEC, N_), dtype=torch.float32, device=dev)
+    y2 = torch.empty((M_PRE, N_), dtype=torch.float32, device=dev)
+    hi = torch.empty((M_PRE, K_), dtype=torch.int16, device=dev)
+    lo = torch.empty((M_PRE, K_), dtype=torch.int16, device=dev)
+
+    def check(st, what):
+        if st != cf.OK:
+            raise RuntimeError(f"{what}: {cf.cfp32_status_string(st)}")
+
+    def step(s, ev=None):
+        w = Ws[s % len(Ws)].data_ptr()
+        if ev: ev[0].record(stream)
+        check(cf.cfp32_linear(x1.data_ptr(), K_, w, N_, y1.data_ptr(), N_, M_DEC, N_, K_, None, 0, sh), "decode")
+        if ev: ev[1].record(stream)
+        check(cf.cfp32_split(x2.data_ptr(), K_, hi.data_ptr(), lo.data_ptr(), K_, M_PRE, K_, sh), "split")
+        if ev: ev[2].record(stream)
+        check(cf.cfp32_gemm(hi.data_ptr(), lo.data_ptr(), K_, w, N_, y2.data_ptr(), None, None, N_,
+                            M_PRE, N_, K_, sh), "gemm")
+        if ev: ev[3].record(stream)
+
+    for s in range(args.warmup):
+        step(s)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s, events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+
+    def avg_us(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in events) / len(events) * 1e3
+
+    dec_us, split_us, gemm_us = avg_us(0, 1), avg_us(1, 2), avg_us(2, 3)
+    flops_step = 2.0 * (M_DEC + M_PRE) * K_ * N_
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    dec_bytes = K_ * N_ * 2 + M_DEC * K_ * 4 + M_DEC * N_ * 4
+    split_bytes = M_PRE * K_ * (4 + 2 + 2)
+    gemm_mfma_flops = 4.0 * M_PRE * N_ * K_          # both FP16 products
+    gemm_tf16 = gemm_mfma_flops / (gemm_us * 1e-6) / 1e12
+    traffic = measured_traffic()
+
+    # -- the two headline kernels on their own -------------------------------
+    def timed(fn, n, warm=3):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    gemv_us = timed(lambda i: check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y1.data_ptr(), N_,
+                                                    M_DEC, N_, K_, None, 0, sh), "decode"), 100)
+    sq = workloads.square()
+    xs = torch.from_numpy(sq.A[0]).to(dev)
+    ws = torch.from_numpy(sq.W.view(np.int16)).to(dev)
+    hs = torch.empty((4096, 4096), dtype=torch.int16, device=dev)
+    ls = torch.empty((4096, 4096), dtype=torch.int16, device=dev)
+    ys = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+    check(cf.cfp32_split(xs.data_ptr(), 4096, hs.data_ptr(), ls.data_ptr(), 4096, 4096, 4096, sh), "split")
+    sq_us = timed(lambda i: check(cf.cfp32_gemm(hs.data_ptr(), ls.data_ptr(), 4096, ws.data_ptr(), 4096,
+                                                ys.data_ptr(), None, None, 4096, 4096, 4096, 4096, sh), "gemm"), 50)
+    torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA x2 + f32 accumulate (compensated f32)",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV 1x4096x14336 + FFN GEMM 8192x4096x14336, shared FP16 W",
+                   "M_decode": M_DEC, "M_prefill": M_PRE, "K": K_, "N": N_, "seed": 4,
+                   "w_copies_rotated": len(Ws)},
+        "roofline": {"bound": "mfma", "kernel": "dual-product GEMM 8192x4096x14336",
+                     "achieved": round(gemm_tf16, 1), "peak": round(PEAK_FP16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(gemm_tf16 / PEAK_FP16_TFLOPS, 4),
+                     "traffic": traffic},
+        "breakdown": {
+            "decode_gemv_us": round(dec_us, 2),
+            "decode_gemv_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+            "split_us": round(split_us, 2),
+            "split_GBps": round(split_bytes / (split_us * 1e-6) / 1e9, 1),
+            "gemm_us": round(gemm_us, 2),
+            "gemm_tflops_fp32eq": round(gemm_mfma_flops / 2 / (gemm_us * 1e-6) / 1e12, 1),
+            "gemm_frac_fp16_peak": round(gemm_tf16 / PEAK_FP16_TFLOPS, 4),
+        },
+        "headline": {
+            "gemm_4096x4096x4096_us": round(sq_us, 2),
+            "gemm_4096_tflops_fp32eq": round(2 * 4096 ** 3 / (sq_us * 1e-6) / 1e12, 1),
+            "gemm_4096_frac_fp16_peak": round(4 * 4096 ** 3 / (sq_us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "gemv_1x4096x14336_us": round(gemv_us, 2),
+            "gemv_GBps": round(dec_bytes / (gemv_us * 1e-6) / 1e9, 1),
+            "gemv_frac_hbm": round(dec_bytes / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "torch": torch.__version__,
+                   "hip": getattr(torch.version, "hip", None)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A1, A2, W, args.cpu_rows_per_thread)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

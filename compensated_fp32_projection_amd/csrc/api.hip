@@ -1,0 +1,171 @@
+// C ABI of libcfp32 (declared in include/cfp32.h): argument validation,
+// the per-device architecture check, workspace layout and path selection.
+// Every call validates all of its arguments before it enqueues anything.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <limits>
+
+#include "../../include/cfp32.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = something else.
+std::atomic<int> g_arch_state[kMaxDevices];
+
+constexpr int64_t kMaxDim = std::numeric_limits<int64_t>::max() / 4;
+
+cfp32_status hip_fail(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return CFP32_ERR_HIP;
+}
+
+// The current device must be gfx950.  The answer is cached per device.
+cfp32_status check_device()
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return CFP32_ERR_UNSUPPORTED_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return CFP32_ERR_UNSUPPORTED_DEVICE;
+    int state = g_arch_state[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            g_last_hip_error = (int)e;
+            return CFP32_ERR_UNSUPPORTED_DEVICE;
+        }
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? CFP32_OK : CFP32_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool dims_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && a <= kMaxDim && b <= kMaxDim; }
+
+// rows x ld elements must be addressable with 64-bit offsets.
+bool extent_ok(int64_t rows, int64_t ld) { return rows == 0 || ld <= kMaxDim / rows; }
+
+cfp32_status launched(hipError_t e) { return e == hipSuccess ? CFP32_OK : hip_fail(e); }
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout for M > 8: the hi plane, then the lo plane, each
+// [M, ldh] FP16 with ldh = K rounded up to 8 (16-byte rows), each starting
+// on a 256-byte boundary of the (realigned) workspace pointer.
+int64_t split_ld(int64_t K) { return (K + 7) / 8 * 8; }
+
+size_t plane_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)split_ld(K) * 2u, kAlign); }
+
+}  // namespace
+
+extern "C" {
+
+const char *cfp32_status_string(cfp32_status s)
+{
+    switch (s) {
+    case CFP32_OK: return "success";
+    case CFP32_ERR_INVALID_VALUE: return "invalid argument (null pointer, negative size, leading dimension or workspace too small)";
+    case CFP32_ERR_UNSUPPORTED_DEVICE: return "no usable device: the current HIP device is not gfx950 (there is no CPU fallback)";
+    case CFP32_ERR_HIP: return "HIP runtime error (see cfp32_last_hip_error)";
+    }
+    return "unknown status";
+}
+
+int cfp32_last_hip_error(void) { return g_last_hip_error; }
+
+cfp32_status cfp32_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo, int64_t ldh,
+                         int64_t rows, int64_t cols, void *stream)
+{
+    if (!dims_ok(rows, cols)) return CFP32_ERR_INVALID_VALUE;
+    if (rows == 0 || cols == 0) return CFP32_OK;
+    if (!x || !hi || !lo || ldx < cols || ldh < cols) return CFP32_ERR_INVALID_VALUE;
+    if (!extent_ok(rows, ldx) || !extent_ok(rows, ldh)) return CFP32_ERR_INVALID_VALUE;
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_split(x, ldx, hi, lo, ldh, rows, cols, (hipStream_t)stream));
+}
+
+cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
+                         int64_t M, int64_t N, void *stream)
+{
+    if (!dims_ok(M, N)) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if (!c_hi || !c_lo || !y || ldc < N || ldy < N) return CFP32_ERR_INVALID_VALUE;
+    if (!extent_ok(M, ldc) || !extent_ok(M, ldy)) return CFP32_ERR_INVALID_VALUE;
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_merge(c_hi, c_lo, ldc, y, ldy, M, N, (hipStream_t)stream));
+}
+
+cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                        int64_t ldw, float *y, float *c_hi, float *c_lo, int64_t ldc, int64_t M,
+                        int64_t N, int64_t K, void *stream)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if ((c_hi == nullptr) != (c_lo == nullptr)) return CFP32_ERR_INVALID_VALUE;
+    if (!y && !c_hi) return CFP32_ERR_INVALID_VALUE;
+    if (ldc < N || !extent_ok(M, ldc)) return CFP32_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!a_hi || !a_lo || !w || lda < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, lda) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+    }
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_gemm(a_hi, a_lo, lda, w, ldw, y, ldc, c_hi, c_lo, ldc, M, N, K,
+                                       (hipStream_t)stream));
+}
+
+size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return 0;
+    if (M <= cfp32::kGemvMaxRows || N == 0 || K == 0) return 0;
+    if (!extent_ok(M, split_ld(K))) return 0;
+    return 2 * plane_bytes(M, K) + kAlign;  // + slack to realign the caller's pointer
+}
+
+cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
+                          int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if (!y || ldy < N || !extent_ok(M, ldy)) return CFP32_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!x || !w || ldx < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+    }
+    const size_t need = cfp32_linear_workspace_bytes(M, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return CFP32_ERR_INVALID_VALUE;
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (M <= cfp32::kGemvMaxRows) return launched(cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, s));
+
+    if (K == 0)  // nothing to split: the product of an empty sum is +0
+        return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
+                                           N, 0, s));
+
+    const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
+    uint16_t *hi = reinterpret_cast<uint16_t *>(base);
+    uint16_t *lo = reinterpret_cast<uint16_t *>(base + plane_bytes(M, K));
+    const int64_t ldh = split_ld(K);
+    hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, s);
+    if (e != hipSuccess) return hip_fail(e);
+    return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Split and merge kernels (laya.cpp Vulkan guide, split/merge paragraph: each
+// runs as a single dispatch).  Both are elementwise and bound by HBM
+// bandwidth: the split reads 4 bytes and writes 2 + 2 per element, the merge
+// reads 8 and writes 4.  Threads of a block cover consecutive columns of one
+// row, so every wave reads and writes contiguous runs; rows go to grid.y.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace cfp32 {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxGridY = 65535;
+
+// VEC: cols, ldx, ldh multiples of 4 and pointers aligned, so each thread
+// moves one 16-byte FP32 group and two 8-byte FP16 groups.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void split_kernel(const float *__restrict__ x, int64_t ldx,
+                                                         uint16_t *__restrict__ hi,
+                                                         uint16_t *__restrict__ lo, int64_t ldh,
+                                                         int64_t rows, int64_t cols)
+{
+    constexpr int kPer = VEC ? 4 : 1;
+    const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (c >= cols) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        if constexpr (VEC) {
+            const float4 v = *reinterpret_cast<const float4 *>(x + r * ldx + c);
+            _Float16 h0, h1, h2, h3, l0, l1, l2, l3;
+            split_value(v.x, h0, l0);
+            split_value(v.y, h1, l1);
+            split_value(v.z, h2, l2);
+            split_value(v.w, h3, l3);
+            *reinterpret_cast<half4_t *>(hi + r * ldh + c) = half4_t{h0, h1, h2, h3};
+            *reinterpret_cast<half4_t *>(lo + r * ldh + c) = half4_t{l0, l1, l2, l3};
+        } else {
+            _Float16 h, l;
+            split_value(x[r * ldx + c], h, l);
+            hi[r * ldh + c] = __builtin_bit_cast(uint16_t, h);
+            lo[r * ldh + c] = __builtin_bit_cast(uint16_t, l);
+        }
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void merge_kernel(const float *__restrict__ c_hi,
+                                                         const float *__restrict__ c_lo, int64_t ldc,
+                                                         float *__restrict__ y, int64_t ldy,
+                                                         int64_t rows, int64_t cols)
+{
+    constexpr int kPer = VEC ? 4 : 1;
+    const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
+    if (c >= cols) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        if constexpr (VEC) {
+            const float4 a = *reinterpret_cast<const float4 *>(c_hi + r * ldc + c);
+            const float4 b = *reinterpret_cast<const float4 *>(c_lo + r * ldc + c);
+            float4 o;
+            o.x = merge_value(a.x, b.x);
+            o.y = merge_value(a.y, b.y);
+            o.z = merge_value(a.z, b.z);
+            o.w = merge_value(a.w, b.w);
+            *reinterpret_cast<float4 *>(y + r * ldy + c) = o;
+        } else {
+            y[r * ldy + c] = merge_value(c_hi[r * ldc + c], c_lo[r * ldc + c]);
+        }
+    }
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Column groups go to grid.x (at most 2^31 - 1 blocks: cols < 2^39 per row).
+dim3 grid_for(int64_t rows, int64_t cols, int per)
+{
+    const int64_t groups = (cols + per - 1) / per;
+    const int64_t bx = (groups + kThreads - 1) / kThreads;
+    const int64_t by = rows < kMaxGridY ? rows : kMaxGridY;
+    return dim3((unsigned)bx, (unsigned)by, 1);
+}
+
+}  // namespace
+
+hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo, int64_t ldh,
+                        int64_t rows, int64_t cols, hipStream_t stream)
+{
+    if ((cols + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && (ldh % 4 == 0) && aligned(x, 16) &&
+                     aligned(hi, 8) && aligned(lo, 8);
+    if (vec) {
+        split_kernel<true><<<grid_for(rows, cols, 4), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols);
+    } else {
+        split_kernel<false><<<grid_for(rows, cols, 1), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
+                        int64_t rows, int64_t cols, hipStream_t stream)
+{
+    if ((cols + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const bool vec = (cols % 4 == 0) && (ldc % 4 == 0) && (ldy % 4 == 0) && aligned(c_hi, 16) &&
+                     aligned(c_lo, 16) && aligned(y, 16);
+    if (vec) {
+        merge_kernel<true><<<grid_for(rows, cols, 4), kThreads, 0, stream>>>(c_hi, c_lo, ldc, y, ldy, rows, cols);
+    } else {
+        merge_kernel<false><<<grid_for(rows, cols, 1), kThreads, 0, stream>>>(c_hi, c_lo, ldc, y, ldy, rows, cols);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cfp32

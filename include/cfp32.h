@@ -1,0 +1,141 @@
+/*
+ * cfp32.h -- C ABI of libcfp32, the compensated-FP32 projection for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (laya.cpp Vulkan backend guide, docs/vulkan.md, compensated-FP32
+ * paragraph and the split/merge paragraph that follows it): an FP32
+ * projection input x is split into two FP16 parts,
+ *
+ *     hi = RNE16(x),   lo = RNE16((x - hi) * 1024)
+ *
+ * (round to nearest even, FP16 subnormals kept; the 1024 scale keeps the
+ * residual away from FP16 underflow without overflowing it, per the guide's
+ * validation paragraph on large activations), both parts are multiplied by
+ * the FP16 weights with FP32 accumulators,
+ *
+ *     C_hi = A_hi W,   C_lo = A_lo W,
+ *
+ * and the two products are combined once, in FP32:
+ *
+ *     y = C_hi + C_lo / 1024.
+ *
+ * The guide runs the split and the merge as one dispatch each; these calls
+ * map onto that: cfp32_split, cfp32_gemm (two products sharing each W tile,
+ * merge fused into its epilogue) and cfp32_merge, plus cfp32_linear, which
+ * runs the whole projection (for M <= 8 as one fused kernel).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Matrices are row-major; every ld* is a leading dimension in elements
+ *   (the distance between consecutive rows) and must be >= the row length.
+ * - FP16 data travels as IEEE binary16 bit patterns in uint16_t.
+ * - All pointers are device memory owned by the caller.  The library never
+ *   allocates, frees, synchronises or prints.  No alignment is required;
+ *   kernels use wide loads only where the pointers and ld allow them.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Calls are asynchronous and ordered on that stream.  Execution faults
+ *   surface at the caller's next synchronisation.
+ * - Arguments are validated before anything is enqueued.  A call that
+ *   returns an error has enqueued nothing.
+ * - M == 0 or N == 0 (rows == 0 or cols == 0 for split) is a no-op that
+ *   returns CFP32_OK.  K == 0 writes +0 to every output element.
+ * - The current HIP device must be gfx950; otherwise
+ *   CFP32_ERR_UNSUPPORTED_DEVICE is returned.  There is no CPU fallback
+ *   (the guide treats an unavailable backend as an error, never a silent
+ *   fallback).
+ * - Outputs must not overlap inputs.
+ * - The library keeps no mutable state besides a per-device cache of the
+ *   architecture check; calls from several threads are safe.
+ */
+#ifndef CFP32_H
+#define CFP32_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define CFP32_API __attribute__((visibility("default")))
+#else
+#define CFP32_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CFP32_OK = 0,
+    CFP32_ERR_INVALID_VALUE = 1,      /* null pointer, negative size, ld too small, workspace too small, size overflow */
+    CFP32_ERR_UNSUPPORTED_DEVICE = 2, /* no HIP device, or the current one is not gfx950 */
+    CFP32_ERR_HIP = 3                 /* a HIP runtime call or kernel launch failed; see cfp32_last_hip_error */
+} cfp32_status;
+
+/* Static, NUL-terminated description of a status code. */
+CFP32_API const char *cfp32_status_string(cfp32_status s);
+
+/* hipError_t value behind the last CFP32_ERR_HIP (or CFP32_ERR_UNSUPPORTED_DEVICE
+ * caused by a failing device query) returned on the calling thread; 0 if none. */
+CFP32_API int cfp32_last_hip_error(void);
+
+/* Split (guide: split/merge paragraph).
+ *   x   : FP32 [rows, cols], leading dimension ldx >= cols.
+ *   hi  : FP16 bits [rows, cols], leading dimension ldh >= cols; hi = RNE16(x).
+ *   lo  : FP16 bits [rows, cols], same ldh; lo = RNE16((x - hi) * 1024).
+ * Bit-exact: FP16 and FP32 subnormals are kept, ties go to even, -0 gives
+ * (hi, lo) = (-0, +0).  Out-of-domain inputs follow IEEE: |x| >= 65520 gives
+ * hi = +-inf and lo = -+inf; inf or NaN input gives a NaN lo (and hi = x for
+ * inf, NaN for NaN).  One kernel launch. */
+CFP32_API cfp32_status cfp32_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo, int64_t ldh,
+                         int64_t rows, int64_t cols, void *stream);
+
+/* Dual-product GEMM with fused merge (guide: compensated-FP32 paragraph).
+ *   a_hi, a_lo : FP16 bits [M, K], leading dimension lda >= K (the split planes).
+ *   w          : FP16 bits [K, N], leading dimension ldw >= N (the weights, exact).
+ *   y          : FP32 [M, N] or NULL; y = C_hi + C_lo / 1024, merged in FP32.
+ *   c_hi, c_lo : FP32 [M, N] or both NULL; the two products before merging.
+ *   ldc        : leading dimension (>= N) of every non-NULL output.
+ * At least one of y and (c_hi, c_lo) must be given; c_hi and c_lo are given
+ * together or not at all.  Both products accumulate in FP32 (FP16 x FP16
+ * products are exact in FP32); they are merged once, after both K-reductions,
+ * so y equals the FP32 merge of the c_hi, c_lo the same call writes.  The
+ * summation order along K is fixed by the kernel, so repeated calls give
+ * identical bits.  One kernel launch. */
+CFP32_API cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,
+                        const uint16_t *w, int64_t ldw,
+                        float *y, float *c_hi, float *c_lo, int64_t ldc,
+                        int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Standalone merge (guide: split/merge paragraph; one dispatch).
+ *   c_hi, c_lo : FP32 [M, N], leading dimension ldc >= N.
+ *   y          : FP32 [M, N], leading dimension ldy >= N.
+ * y = fl32(c_hi + fl32(c_lo * 2^-10)), bit-exact, no fused multiply-add. */
+CFP32_API cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
+                         int64_t M, int64_t N, void *stream);
+
+/* Bytes of device workspace cfp32_linear needs for this shape (0 when none
+ * is needed: M <= 8, or an empty problem).  Returns 0 for negative sizes. */
+CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* The whole projection y = x W (guide: compensated-FP32 paragraph; small
+ * projections run at their real row count, with no padding of M).
+ *   x   : FP32 [M, K], leading dimension ldx >= K.
+ *   w   : FP16 bits [K, N], leading dimension ldw >= N.
+ *   y   : FP32 [M, N], leading dimension ldy >= N.
+ *   workspace, workspace_bytes : device scratch of at least
+ *         cfp32_linear_workspace_bytes(M, N, K) bytes (may be NULL when that
+ *         is 0).  Its contents on entry are ignored; it must not be used by
+ *         another call until this call's work on `stream` has completed.
+ * M <= 8: one fused kernel (split in registers, both products, merge).
+ * M  > 8: cfp32_split into the workspace, then cfp32_gemm with the merged
+ *         epilogue (two launches).
+ * Results satisfy |y - y_exact| <= 1e-5 * sum_k |x_k w_k| for inputs within
+ * the split's domain (|x| < 65520). */
+CFP32_API cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
+                          float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFP32_H */

@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every function include/cfp32.h
+declares, and its host-side argument checks run before any device work.
+
+No kernel is launched here.  Calls that fail validation, or that are empty,
+return before the library touches the GPU; on a machine without a gfx950 GPU
+a valid call must report CFP32_ERR_UNSUPPORTED_DEVICE (there is no CPU
+fallback).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compensated_fp32_projection_amd as cf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cfp32.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CFP32_API\s+[\w\s\*]*?\b(cfp32_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cf.LIB_PATH):
+        from compensated_fp32_projection_amd import build
+        build.build()
+    return cf.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(cf.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for s in (cf.OK, cf.ERR_INVALID_VALUE, cf.ERR_UNSUPPORTED_DEVICE, cf.ERR_HIP):
+        assert cf.cfp32_status_string(s)
+    assert cf.cfp32_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20  # never dereferenced: these calls fail or return before any device work
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    E = cf.ERR_INVALID_VALUE
+    # negative sizes
+    assert cf.cfp32_split(FAKE, 4, FAKE, FAKE, 4, -1, 4, None) == E
+    assert cf.cfp32_gemm(FAKE, FAKE, 4, FAKE, 4, FAKE, None, None, 4, 4, 4, -4, None) == E
+    # null pointers
+    assert cf.cfp32_split(None, 4, FAKE, FAKE, 4, 2, 4, None) == E
+    assert cf.cfp32_merge(FAKE, None, 4, FAKE, 4, 2, 4, None) == E
+    assert cf.cfp32_linear(FAKE, 8, None, 8, FAKE, 8, 2, 8, 8, None, 0, None) == E
+    # leading dimension below the row length
+    assert cf.cfp32_split(FAKE, 3, FAKE, FAKE, 4, 2, 4, None) == E
+    assert cf.cfp32_gemm(FAKE, FAKE, 7, FAKE, 8, FAKE, None, None, 8, 4, 8, 8, None) == E
+    assert cf.cfp32_merge(FAKE, FAKE, 8, FAKE, 7, 2, 8, None) == E
+    # gemm: no output, or only one of c_hi / c_lo
+    assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, None, None, 8, 4, 8, 8, None) == E
+    assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, FAKE, None, 8, 4, 8, 8, None) == E
+    # linear: workspace missing or too small for M > 8
+    need = cf.cfp32_linear_workspace_bytes(64, 64, 64)
+    assert need > 0
+    assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, 64, 64, 64, None, 0, None) == E
+    assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, 64, 64, 64, FAKE, need - 1, None) == E
+    # sizes whose extent overflows 64-bit offsets
+    big = 1 << 40
+    assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
+
+
+def test_workspace_sizes(lib):
+    assert cf.cfp32_linear_workspace_bytes(8, 4096, 4096) == 0        # fused small-M path
+    assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
+    assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0
+    assert cf.cfp32_linear_workspace_bytes(-1, 10, 10) == 0
+    # two FP16 planes of M x roundup(K, 8), 256-byte aligned, plus alignment slack
+    assert cf.cfp32_linear_workspace_bytes(9, 5, 1) == 2 * 256 + 256
+    assert cf.cfp32_linear_workspace_bytes(4096, 4096, 4096) == 2 * 4096 * 4096 * 2 + 256
+
+
+def test_empty_problems_are_no_ops(lib):
+    assert cf.cfp32_split(None, 0, None, None, 0, 0, 5, None) == cf.OK
+    assert cf.cfp32_gemm(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, None) == cf.OK
+    assert cf.cfp32_merge(None, None, 0, None, 0, 4, 0, None) == cf.OK
+    assert cf.cfp32_linear(None, 0, None, 0, None, 0, 0, 8, 8, None, 0, None) == cf.OK
+
+
+def test_no_cpu_fallback_without_gfx950():
+    """With no gfx950 device visible, a valid call must refuse to run."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the refusal path needs a machine without one")
+    cf.load_library()
+    st = cf.cfp32_split(FAKE, 4, FAKE, FAKE, 4, 1, 4, None)
+    assert st == cf.ERR_UNSUPPORTED_DEVICE
+
+
+def test_binding_raises_without_library(tmp_path, monkeypatch):
+    """The Python layer fails loudly when the HIP library is missing."""
+    monkeypatch.setattr(cf, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(cf, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        cf.load_library()

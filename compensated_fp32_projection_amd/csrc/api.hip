@@ -94,7 +94,7 @@ cfp32_status cfp32_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo
     if (!extent_ok(rows, ldx) || !extent_ok(rows, ldh)) return CFP32_ERR_INVALID_VALUE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
-    return launched(cfp32::launch_split(x, ldx, hi, lo, ldh, rows, cols, (hipStream_t)stream));
+    return launched(cfp32::launch_split(x, ldx, hi, lo, ldh, rows, cols, cols, (hipStream_t)stream));
 }
 
 cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
@@ -125,7 +125,7 @@ cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
     return launched(cfp32::launch_gemm(a_hi, a_lo, lda, w, ldw, y, ldc, c_hi, c_lo, ldc, M, N, K,
-                                       (hipStream_t)stream));
+                                       /*a_zero_padded=*/false, (hipStream_t)stream));
 }
 
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -157,15 +157,18 @@ cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_
 
     if (K == 0)  // nothing to split: the product of an empty sum is +0
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
-                                           N, 0, s));
+                                           N, 0, false, s));
 
     const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);
     uint16_t *lo = reinterpret_cast<uint16_t *>(base + plane_bytes(M, K));
     const int64_t ldh = split_ld(K);
-    hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, s);
+    // The planes are written with zeros in columns [K, ldh), so the GEMM may
+    // read whole 16-byte groups past K.
+    hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, ldh, s);
     if (e != hipSuccess) return hip_fail(e);
-    return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, s));
+    return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K,
+                                       /*a_zero_padded=*/true, s));
 }
 
 }  // extern "C"

@@ -93,7 +93,16 @@ __device__ __forceinline__ int w_slot(int kg, int n)
     return T::LDS_A + kg * T::BN + (n ^ ((n >> 3) & 7));
 }
 
-template <class T, bool AL_A, bool AL_W>
+// Offset that no buffer reaches: a raw buffer load at it returns zero and
+// touches no memory, whether or not the scalar offset enters the range check.
+constexpr int kNoOffset = 0x7FFFFFF0;
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+// BUF: every operand is 16-byte aligned and smaller than 2^31 bytes, so full
+// K stages are fetched with raw buffer loads (no per-load branches; rows past
+// M and columns past N read as zero).  The ragged last stage, and every stage
+// of the generic variant, use guarded loads.
+template <class T, bool AL_A, bool AL_W, bool BUF>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 {
     __shared__ uint4 lds[2 * T::LDS_STAGE];
@@ -134,6 +143,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 
     uint4 ra[2][T::A_CHUNKS];
     uint4 rw[T::W_ITERS][8];
+
+    // Buffer-load state (used only when BUF): wave-uniform descriptors and
+    // per-thread byte offsets that do not change from stage to stage; the
+    // stage's k offset travels in the scalar offset.
+    const __amdgpu_buffer_rsrc_t rs_hi =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_hi), 0, (int)(g.M * g.lda * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs_lo =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_lo), 0, (int)(g.M * g.lda * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
+    int voff_a[T::A_CHUNKS];
+    int voff_w[T::W_ITERS];
+    if constexpr (BUF) {
+#pragma unroll
+        for (int i = 0; i < T::A_CHUNKS; ++i) {
+            const int c = tid + kThreads * i;
+            const int64_t gm = m0 + (c >> 3);
+            voff_a[i] = gm < g.M ? (int)((gm * g.lda + 8 * (c & 7)) * 2) : kNoOffset;
+        }
+#pragma unroll
+        for (int j = 0; j < T::W_ITERS; ++j) {
+            const int b = tid + kThreads * j;
+            const int kgw = b / (T::BN / 8), nc = b % (T::BN / 8);
+            const int64_t gn = n0 + 8 * nc;
+            voff_w[j] = gn < g.N ? (int)((8 * kgw * g.ldw + gn) * 2) : kNoOffset;
+        }
+    }
+
+    auto load_stage_buf = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < T::A_CHUNKS; ++i) {
+            ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], (int)(k0 * 2), 0));
+            ra[1][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, voff_a[i], (int)(k0 * 2), 0));
+        }
+#pragma unroll
+        for (int j = 0; j < T::W_ITERS; ++j) {
+            if (tid + kThreads * j < T::W_BLOCKS) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    rw[j][r] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[j], (int)((k0 + r) * g.ldw * 2), 0));
+            }
+        }
+    };
 
     auto load_stage = [&](int64_t k0) {
 #pragma unroll
@@ -197,45 +250,74 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         }
     };
 
-    auto compute_stage = [&](int st) {
-        const uint4 *s = lds + st * T::LDS_STAGE;
+    // Fragments of one 16-deep k-step: A hi/lo rows and W columns.
+    struct Frags {
+        half8_t ah[T::TM], al[T::TM], bw[T::TN];
+    };
+    auto read_frags = [&](const uint4 *s, int ks, Frags &f) {
+        const int kg = 2 * ks + (lane >> 5);
 #pragma unroll
-        for (int ks = 0; ks < kKG / 2; ++ks) {
-            const int kg = 2 * ks + (lane >> 5);
-            half8_t ah[T::TM], al[T::TM], bw[T::TN];
+        for (int i = 0; i < T::TM; ++i) {
+            const int row = wm * T::WTM + i * 32 + (lane & 31);
+            f.ah[i] = __builtin_bit_cast(half8_t, s[a_slot<T>(0, kg, row)]);
+            f.al[i] = __builtin_bit_cast(half8_t, s[a_slot<T>(1, kg, row)]);
+        }
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                const int row = wm * T::WTM + i * 32 + (lane & 31);
-                ah[i] = __builtin_bit_cast(half8_t, s[a_slot<T>(0, kg, row)]);
-                al[i] = __builtin_bit_cast(half8_t, s[a_slot<T>(1, kg, row)]);
-            }
+        for (int j = 0; j < T::TN; ++j) {
+            const int n = wn * T::WTN + j * 32 + (lane & 31);
+            f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot<T>(kg, n)]);
+        }
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
-                const int n = wn * T::WTN + j * 32 + (lane & 31);
-                bw[j] = __builtin_bit_cast(half8_t, s[w_slot<T>(kg, n)]);
+                acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
+                acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
             }
+    };
+    // The fragments of k-step ks+1 are read while the MFMAs of ks run.
+    auto compute_stage = [&](int st) {
+        const uint4 *s = lds + st * T::LDS_STAGE;
+        Frags f[2];
+        read_frags(s, 0, f[0]);
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j) {
-                    acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bw[j], acc_hi[i][j], 0, 0, 0);
-                    acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bw[j], acc_lo[i][j], 0, 0, 0);
-                }
+        for (int ks = 0; ks < kKG / 2; ++ks) {
+            if (ks + 1 < kKG / 2) read_frags(s, ks + 1, f[(ks + 1) & 1]);
+            mfmas(f[ks & 1]);
         }
     };
 
+    // K loop.  Stage kt is multiplied out of LDS buffer kt&1 while stage kt+1
+    // is fetched into registers; one barrier per stage.  Full stages use the
+    // buffer loads, so the main loop has no branch; the ragged last stage (if
+    // K is not a multiple of 64) is peeled off and uses guarded loads.
     const int64_t nk = (g.K + kBK - 1) / kBK;
-    if (nk > 0) {
-        load_stage(0);
+    const int64_t nk_full = BUF ? g.K / kBK : 0;
+    if (nk == 0) {
+        // K == 0: nothing to accumulate; the epilogue writes +0.
+    } else {
+        if (nk_full > 0)
+            load_stage_buf(0);
+        else
+            load_stage(0);
         store_stage(0);
-    }
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) load_stage((kt + 1) * kBK);
-        compute_stage(cur);
-        if (kt + 1 < nk) store_stage(cur ^ 1);
         __syncthreads();
+        int64_t kt = 0;
+        for (; kt + 1 < nk_full; ++kt) {
+            load_stage_buf((kt + 1) * kBK);
+            compute_stage((int)(kt & 1));
+            store_stage((int)((kt + 1) & 1));
+            __syncthreads();
+        }
+        for (; kt + 1 < nk; ++kt) {
+            load_stage((kt + 1) * kBK);
+            compute_stage((int)(kt & 1));
+            store_stage((int)((kt + 1) & 1));
+            __syncthreads();
+        }
+        compute_stage((int)(kt & 1));
     }
 
     // --- epilogue: 32x32 accumulator layout of v_mfma_f32_32x32x16_f16:
@@ -270,15 +352,21 @@ hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const bool al_a = (g.lda % 8 == 0) && aligned16(g.a_hi) && aligned16(g.a_lo);
     const bool al_w = (g.ldw % 8 == 0) && aligned16(g.w);
+    // Buffer offsets are 32-bit: every byte offset a thread forms, including a
+    // tile's overhang past M and N, must stay below kNoOffset.
+    constexpr int64_t kLim = kNoOffset - (1 << 20);
+    const bool fits = (g.M + T::BM) * g.lda * 2 < kLim && (g.K + kBK) * g.ldw * 2 + (int64_t)T::BN * 2 < kLim;
     const dim3 grid((unsigned)blocks);
-    if (al_a && al_w)
-        gemm_kernel<T, true, true><<<grid, kThreads, 0, stream>>>(g);
+    if (al_a && al_w && fits)
+        gemm_kernel<T, true, true, true><<<grid, kThreads, 0, stream>>>(g);
+    else if (al_a && al_w)
+        gemm_kernel<T, true, true, false><<<grid, kThreads, 0, stream>>>(g);
     else if (al_a)
-        gemm_kernel<T, true, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, false, false><<<grid, kThreads, 0, stream>>>(g);
     else if (al_w)
-        gemm_kernel<T, false, true><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, true, false><<<grid, kThreads, 0, stream>>>(g);
     else
-        gemm_kernel<T, false, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, false, false><<<grid, kThreads, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -294,11 +382,16 @@ int64_t tiles_of(int64_t M, int64_t N)
 // (256 CUs); below that, the smallest tile, which has the most blocks.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream)
+                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream)
 {
     GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K};
     constexpr int64_t kCus = 256;
-    if (tiles_of<TileLarge>(M, N) >= kCus) return launch_tile<TileLarge>(g, stream);
+    if (tiles_of<TileLarge>(M, N) >= kCus) {
+        const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
+                                             a_zero_padded, stream);
+        if (e != hipErrorNotSupported) return e;
+        return launch_tile<TileLarge>(g, stream);
+    }
     if (tiles_of<TileMedium>(M, N) >= kCus) return launch_tile<TileMedium>(g, stream);
     return launch_tile<TileSmall>(g, stream);
 }

@@ -26,19 +26,22 @@ namespace cfp32 {
 
 namespace {
 
-constexpr int kGemvThreads = 512;
-constexpr int kGemvNB = 64;   // output columns per block
-constexpr int kGemvU = 8;     // loads in flight per thread
+constexpr int kNoOffset = 0x7FFFFFF0;      // a raw buffer load here reads zero
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 
-template <int MR, bool AL>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restrict__ x, int64_t ldx,
-                                                            const uint16_t *__restrict__ w, int64_t ldw,
-                                                            float *__restrict__ y, int64_t ldy,
-                                                            int64_t N, int64_t K)
+// THREADS threads own NB output columns; U loads per thread in flight.
+// BUF: W is 16-byte aligned with ldw % 8 == 0 and under 2^31 bytes, so W is
+// read with raw buffer loads whose out-of-range lanes read zero (no branches,
+// so all U loads of a thread are in flight together); otherwise W is read
+// through the guarded element path.
+template <int MR, bool BUF, int THREADS, int NB, int U>
+__global__ __launch_bounds__(THREADS) void gemv_kernel(const float *__restrict__ x, int64_t ldx,
+                                                       const uint16_t *__restrict__ w, int64_t ldw,
+                                                       float *__restrict__ y, int64_t ldy, int64_t N, int64_t K)
 {
-    constexpr int CH = kGemvNB / 8;
-    constexpr int KL = kGemvThreads / CH;
-    constexpr int WAVES = kGemvThreads / 64;
+    constexpr int CH = NB / 8;
+    constexpr int KL = THREADS / CH;
+    constexpr int WAVES = THREADS / 64;
     static_assert(CH <= 64 && (CH & (CH - 1)) == 0, "column groups are a power of two within a wave");
 
     __shared__ float red[WAVES][CH][MR][8][2];
@@ -46,8 +49,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
     const int tid = threadIdx.x;
     const int c = tid % CH;
     const int kl = tid / CH;
-    const int64_t n0 = (int64_t)blockIdx.x * kGemvNB;
+    const int64_t n0 = (int64_t)blockIdx.x * NB;
     const int64_t n = n0 + 8 * c;
+
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0, BUF ? (int)(K * ldw * 2) : 0, kBufferWord3);
 
     float sh[MR][8], sl[MR][8];
 #pragma unroll
@@ -55,17 +61,29 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
 
-    for (int64_t kb = kl; kb < K; kb += (int64_t)KL * kGemvU) {
-        uint4 wv[kGemvU];
+    for (int64_t kb = kl; kb < K; kb += (int64_t)KL * U) {
+        // x first, then W: the vector-memory counter drains in issue order, so
+        // one wait for the last W load covers every x of the batch.
+        float xv[U][MR];
 #pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t k = kb + (int64_t)u * KL;
-            wv[u] = (k < K) ? load_row8<AL>(w + k * ldw, n, N) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) xv[u][m] = (k < K) ? x[m * ldx + k] : 0.0f;
+        }
+        uint4 wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = kb + (int64_t)u * KL;
+            if constexpr (BUF) {
+                const int off = (k < K && n < N) ? (int)((k * ldw + n) * 2) : kNoOffset;
+                wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0));
+            } else {
+                wv[u] = (k < K) ? load_row8<false>(w + k * ldw, n, N) : make_uint4(0, 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kGemvU; ++u) {
-            const int64_t k = kb + (int64_t)u * KL;
-            if (k >= K) break;
+        for (int u = 0; u < U; ++u) {
             const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
             float wf[8];
 #pragma unroll
@@ -73,7 +91,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 _Float16 h16, l16;
-                split_value(x[m * ldx + k], h16, l16);
+                split_value(xv[u][m], h16, l16);
                 const float h = (float)h16, l = (float)l16;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -86,13 +104,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
 
     // Butterfly over the k-lanes of this wave (lanes c, c+CH, c+2CH, ...).
 #pragma unroll
-    for (int s = CH; s < 64; s <<= 1)
+    for (int sft = CH; sft < 64; sft <<= 1)
 #pragma unroll
         for (int m = 0; m < MR; ++m)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                sh[m][e] += __shfl_xor(sh[m][e], s, 64);
-                sl[m][e] += __shfl_xor(sl[m][e], s, 64);
+                sh[m][e] += __shfl_xor(sh[m][e], sft, 64);
+                sl[m][e] += __shfl_xor(sl[m][e], sft, 64);
             }
     const int lane = tid & 63, wave = tid >> 6;
     if (lane < CH) {
@@ -107,8 +125,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
     __syncthreads();
 
     // Waves in index order, then the merge; one thread per output.
-    for (int o = tid; o < MR * kGemvNB; o += kGemvThreads) {
-        const int m = o / kGemvNB, col = o % kGemvNB;
+    for (int o = tid; o < MR * NB; o += THREADS) {
+        const int m = o / NB, col = o % NB;
         const int64_t gn = n0 + col;
         if (gn >= N) continue;
         float th = 0.0f, tl = 0.0f;
@@ -121,19 +139,33 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const float *__restr
     }
 }
 
+template <int MR, int THREADS, int NB, int U>
+hipError_t launch_cfg(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                      int64_t N, int64_t K, hipStream_t stream)
+{
+    const int64_t blocks = (N + NB - 1) / NB;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
+    const bool buf = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
+                     (K + 1) * ldw * 2 < kNoOffset - (1 << 20);
+    if (buf)
+        gemv_kernel<MR, true, THREADS, NB, U><<<grid, THREADS, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
+    else
+        gemv_kernel<MR, false, THREADS, NB, U><<<grid, THREADS, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
+    return hipGetLastError();
+}
+
+// Launch shape per row count: 1024 threads keep more loads in flight while
+// the accumulators are few; from three rows on, 512 threads leave each
+// thread enough registers for 2 x 8 x M accumulators.
 template <int MR>
 hipError_t launch_rows(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                        int64_t N, int64_t K, hipStream_t stream)
 {
-    const int64_t blocks = (N + kGemvNB - 1) / kGemvNB;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks);
-    const bool al = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
-    if (al)
-        gemv_kernel<MR, true><<<grid, kGemvThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
+    if constexpr (MR <= 2)
+        return launch_cfg<MR, 1024, 64, 8>(x, ldx, w, ldw, y, ldy, N, K, stream);
     else
-        gemv_kernel<MR, false><<<grid, kGemvThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
-    return hipGetLastError();
+        return launch_cfg<MR, 512, 64, 8>(x, ldx, w, ldw, y, ldy, N, K, stream);
 }
 
 }  // namespace

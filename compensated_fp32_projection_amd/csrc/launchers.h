@@ -8,16 +8,25 @@
 
 namespace cfp32 {
 
+// Columns [cols, cols_out) of hi and lo are written as +0 (zero padding for
+// the GEMM's 16-byte loads); cols_out == cols for the public split.
 hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo, int64_t ldh,
-                        int64_t rows, int64_t cols, hipStream_t stream);
+                        int64_t rows, int64_t cols, int64_t cols_out, hipStream_t stream);
 
 hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
                         int64_t rows, int64_t cols, hipStream_t stream);
 
 // y (ldy) and/or c_hi, c_lo (ldc) outputs; any of them may be null.
+// a_zero_padded: A's columns from K to the next multiple of 8 hold +0.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
+
+// LDS-DMA variant for aligned operands (gemm_dma.hip); hipErrorNotSupported
+// when the operands do not allow it, in which case nothing was enqueued.
+hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                           int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
 
 // Fused split + both products + merge for 1 <= M <= 8.
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,

@@ -19,13 +19,21 @@ template <bool VEC>
 __global__ __launch_bounds__(kThreads) void split_kernel(const float *__restrict__ x, int64_t ldx,
                                                          uint16_t *__restrict__ hi,
                                                          uint16_t *__restrict__ lo, int64_t ldh,
-                                                         int64_t rows, int64_t cols)
+                                                         int64_t rows, int64_t cols, int64_t cols_out)
 {
     constexpr int kPer = VEC ? 4 : 1;
     const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kPer;
-    if (c >= cols) return;
+    if (c >= cols_out) return;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        if constexpr (VEC) {
+        if (c >= cols) {  // zero padding (whole group: cols and cols_out are multiples of kPer)
+            if constexpr (VEC) {
+                *reinterpret_cast<half4_t *>(hi + r * ldh + c) = half4_t{};
+                *reinterpret_cast<half4_t *>(lo + r * ldh + c) = half4_t{};
+            } else {
+                hi[r * ldh + c] = 0;
+                lo[r * ldh + c] = 0;
+            }
+        } else if constexpr (VEC) {
             const float4 v = *reinterpret_cast<const float4 *>(x + r * ldx + c);
             _Float16 h0, h1, h2, h3, l0, l1, l2, l3;
             split_value(v.x, h0, l0);
@@ -82,15 +90,17 @@ dim3 grid_for(int64_t rows, int64_t cols, int per)
 }  // namespace
 
 hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo, int64_t ldh,
-                        int64_t rows, int64_t cols, hipStream_t stream)
+                        int64_t rows, int64_t cols, int64_t cols_out, hipStream_t stream)
 {
-    if ((cols + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && (ldh % 4 == 0) && aligned(x, 16) &&
-                     aligned(hi, 8) && aligned(lo, 8);
+    if ((cols_out + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const bool vec = (cols % 4 == 0) && (cols_out % 4 == 0) && (ldx % 4 == 0) && (ldh % 4 == 0) &&
+                     aligned(x, 16) && aligned(hi, 8) && aligned(lo, 8);
     if (vec) {
-        split_kernel<true><<<grid_for(rows, cols, 4), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols);
+        split_kernel<true><<<grid_for(rows, cols_out, 4), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols,
+                                                                                  cols_out);
     } else {
-        split_kernel<false><<<grid_for(rows, cols, 1), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols);
+        split_kernel<false><<<grid_for(rows, cols_out, 1), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols,
+                                                                                   cols_out);
     }
     return hipGetLastError();
 }

@@ -42,11 +42,15 @@ PEAK_FP16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
 PEAK_HBM_GBS = 8000.0
 K_, N_, M_DEC, M_PRE = 4096, 14336, 1, 8192
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_counters.txt")
+CALIB_BYTES = 512 * 1024 * 1024  # plain device copy of known size, for counter scaling
+GEMM_KERNEL = "gemm_dma_kernel"
+COPY_KERNEL_HINT = "copy"
+PREFILL_GEMM_THREADS = (8192 // 128) * (14336 // 256) * 256
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("gemm.hip", "device_common.h"):
+    for name in ("gemm_dma.hip", "gemm.hip", "tile_order.h", "device_common.h"):
         with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -84,14 +88,93 @@ def cpu_baseline(A1, A2, W, rows_per_thread: int):
                       f"(split + two FP32-accumulated products + merge, OpenMP over rows)"}
 
 
+def _read_counter_csv(path):
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Dispatch_Id"], r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0))
+            per.setdefault(key, {})
+            per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize_counters(fetch_csv, write_csv, out_path, command):
+    """Write the HBM-traffic summary of the GEMM from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the plain copy of CALIB_BYTES in the same run."""
+    lines = [f"# rocprofv3 counter summary: dual-product GEMM 8192x4096x14336 (decode/FFN prefill step)",
+             f"# command: {command}",
+             f"kernel_source_hash: {kernel_source_hash()}"]
+    result = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _read_counter_csv(path)
+        # the prefill GEMM launches 56 x 64 tiles of 256 threads
+        gemm = [v[name] for (d, k, gs), v in per.items() if GEMM_KERNEL in k and name in v
+                and gs == PREFILL_GEMM_THREADS]
+        copy = [v[name] for (d, k, gs), v in per.items() if COPY_KERNEL_HINT in k.lower() and name in v
+                and v[name] * 1024 > CALIB_BYTES * 0.5]
+        if not gemm or not copy:
+            raise SystemExit(f"{path}: no {name} rows for the GEMM or the calibration copy")
+        g = sum(gemm) / len(gemm)
+        c = max(copy)
+        # A device copy reads and writes CALIB_BYTES each.
+        factor = CALIB_BYTES / (c * 1024.0)
+        result[name] = g * 1024.0 * factor
+        lines += [f"{name}_gemm_KiB_per_dispatch: {g:.1f}  (dispatches: {len(gemm)})",
+                  f"{name}_copy_KiB: {c:.1f}  (copy of {CALIB_BYTES} bytes)",
+                  f"{name}_scale_factor: {factor:.4f}",
+                  f"{name}_gemm_bytes_per_launch: {result[name]:.4e}"]
+    total = result["FETCH_SIZE"] + result["WRITE_SIZE"]
+    alg = 8192 * 4096 * 2 * 2 + 4096 * 14336 * 2 + 8192 * 14336 * 4
+    lines += [f"hbm_bytes_per_launch: {total:.4e}",
+              f"algorithmic_bytes_per_launch: {alg:.4e}  (A_hi + A_lo + W + y)",
+              f"traffic_over_algorithmic: {total / alg:.3f}"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(stats_csv, out_path, command):
+    """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# rocprofv3 kernel-trace summary: decode/FFN step, MI355X",
+             f"# command: {command}",
+             f"kernel_source_hash: {kernel_source_hash()}",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} {float(r['MinNs'])/1e3:10.2f} "
+                     f"{float(r['MaxNs'])/1e3:10.2f}  {name}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-per-thread", type=int, default=12)
+    ap.add_argument("--cpu-rows-per-thread", type=int, default=40)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="summarise two rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run (no GPU needed)")
+    ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.profile_command)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.profile_command)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -186,6 +269,13 @@ def main():
     sq_us = timed(lambda i: check(cf.cfp32_gemm(hs.data_ptr(), ls.data_ptr(), 4096, ws.data_ptr(), 4096,
                                                 ys.data_ptr(), None, None, 4096, 4096, 4096, 4096, sh), "gemm"), 50)
     torch.cuda.synchronize()
+
+    if args.calibration_copy:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": METRIC,

@@ -244,6 +244,23 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         read_stage(stage_buf<(S + 1) & 3>(), nxt);
         mfmas(cur[0]);
         mfmas(cur[1]);
+        // Instruction order for the scheduler: the 8 DMA loads and 24 LDS
+        // reads of this step are threaded between the first 16 of its 32
+        // MFMAs (MFMA, load, 2 reads; then MFMA, read), so the matrix pipe is
+        // fed while they issue instead of idling behind a block of them.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the DMA)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     };
 
     Frags fa[2], fb[2];

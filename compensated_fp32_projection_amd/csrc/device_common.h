@@ -16,6 +16,7 @@ namespace cfp32 {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 // The split of one FP32 value (laya.cpp Vulkan guide, split/merge paragraph):
 // hi = RNE16(x); lo = RNE16((x - hi) * 1024).  The FP32 -> FP16 conversion

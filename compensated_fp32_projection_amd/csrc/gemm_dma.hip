@@ -296,10 +296,12 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
                 const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (row >= g.M) continue;
                 const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
-                if (g.y) g.y[row * g.ldy + col] = merge_value(h, l);
+                // Outputs are written once: non-temporal stores keep them from
+                // evicting the A and W panels other tiles still read from L2.
+                if (g.y) __builtin_nontemporal_store(merge_value(h, l), g.y + row * g.ldy + col);
                 if (g.c_hi) {
-                    g.c_hi[row * g.ldc + col] = h;
-                    g.c_lo[row * g.ldc + col] = l;
+                    __builtin_nontemporal_store(h, g.c_hi + row * g.ldc + col);
+                    __builtin_nontemporal_store(l, g.c_lo + row * g.ldc + col);
                 }
             }
         }

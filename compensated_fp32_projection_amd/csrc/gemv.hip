@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kNoOffset = 0x7FFFFFF0;      // a raw buffer load here reads zero
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+constexpr int kStreamAux = 2;             // cache policy "nt": W is read once, do not keep it in cache
 
 // THREADS threads own NB output columns; U loads per thread in flight.
 // BUF: W is 16-byte aligned with ldw % 8 == 0 and under 2^31 bytes, so W is
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const float *__restrict__
             const int64_t k = kb + (int64_t)u * KL;
             if constexpr (BUF) {
                 const int off = (k < K && n < N) ? (int)((k * ldw + n) * 2) : kNoOffset;
-                wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, 0));
+                wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, kStreamAux));
             } else {
                 wv[u] = (k < K) ? load_row8<false>(w + k * ldw, n, N) : make_uint4(0, 0, 0, 0);
             }

@@ -3,6 +3,8 @@
 // bandwidth: the split reads 4 bytes and writes 2 + 2 per element, the merge
 // reads 8 and writes 4.  Threads of a block cover consecutive columns of one
 // row, so every wave reads and writes contiguous runs; rows go to grid.y.
+// Every byte is touched once, so the vector paths use non-temporal loads and
+// stores (streaming cache policy).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -27,21 +29,21 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const float *__restrict
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
         if (c >= cols) {  // zero padding (whole group: cols and cols_out are multiples of kPer)
             if constexpr (VEC) {
-                *reinterpret_cast<half4_t *>(hi + r * ldh + c) = half4_t{};
-                *reinterpret_cast<half4_t *>(lo + r * ldh + c) = half4_t{};
+                __builtin_nontemporal_store(half4_t{}, reinterpret_cast<half4_t *>(hi + r * ldh + c));
+                __builtin_nontemporal_store(half4_t{}, reinterpret_cast<half4_t *>(lo + r * ldh + c));
             } else {
                 hi[r * ldh + c] = 0;
                 lo[r * ldh + c] = 0;
             }
         } else if constexpr (VEC) {
-            const float4 v = *reinterpret_cast<const float4 *>(x + r * ldx + c);
+            const floatx4_t v = __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(x + r * ldx + c));
             _Float16 h0, h1, h2, h3, l0, l1, l2, l3;
-            split_value(v.x, h0, l0);
-            split_value(v.y, h1, l1);
-            split_value(v.z, h2, l2);
-            split_value(v.w, h3, l3);
-            *reinterpret_cast<half4_t *>(hi + r * ldh + c) = half4_t{h0, h1, h2, h3};
-            *reinterpret_cast<half4_t *>(lo + r * ldh + c) = half4_t{l0, l1, l2, l3};
+            split_value(v[0], h0, l0);
+            split_value(v[1], h1, l1);
+            split_value(v[2], h2, l2);
+            split_value(v[3], h3, l3);
+            __builtin_nontemporal_store(half4_t{h0, h1, h2, h3}, reinterpret_cast<half4_t *>(hi + r * ldh + c));
+            __builtin_nontemporal_store(half4_t{l0, l1, l2, l3}, reinterpret_cast<half4_t *>(lo + r * ldh + c));
         } else {
             _Float16 h, l;
             split_value(x[r * ldx + c], h, l);
@@ -62,14 +64,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float *__restrict
     if (c >= cols) return;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
         if constexpr (VEC) {
-            const float4 a = *reinterpret_cast<const float4 *>(c_hi + r * ldc + c);
-            const float4 b = *reinterpret_cast<const float4 *>(c_lo + r * ldc + c);
-            float4 o;
-            o.x = merge_value(a.x, b.x);
-            o.y = merge_value(a.y, b.y);
-            o.z = merge_value(a.z, b.z);
-            o.w = merge_value(a.w, b.w);
-            *reinterpret_cast<float4 *>(y + r * ldy + c) = o;
+            const floatx4_t a = __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(c_hi + r * ldc + c));
+            const floatx4_t b = __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(c_lo + r * ldc + c));
+            const floatx4_t o = {merge_value(a[0], b[0]), merge_value(a[1], b[1]), merge_value(a[2], b[2]),
+                                 merge_value(a[3], b[3])};
+            __builtin_nontemporal_store(o, reinterpret_cast<floatx4_t *>(y + r * ldy + c));
         } else {
             y[r * ldy + c] = merge_value(c_hi[r * ldc + c], c_lo[r * ldc + c]);
         }

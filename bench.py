@@ -45,7 +45,6 @@ COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_c
 CALIB_BYTES = 512 * 1024 * 1024  # plain device copy of known size, for counter scaling
 GEMM_KERNEL = "gemm_dma_kernel"
 COPY_KERNEL_HINT = "copy"
-PREFILL_GEMM_THREADS = (8192 // 128) * (14336 // 256) * 256
 
 
 def kernel_source_hash() -> str:
@@ -109,9 +108,10 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
     result = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         per = _read_counter_csv(path)
-        # the prefill GEMM launches 56 x 64 tiles of 256 threads
+        # the prefill GEMM is the GEMM launch with the largest grid in the run
+        sizes = [gs for (d, k, gs) in per if GEMM_KERNEL in k]
         gemm = [v[name] for (d, k, gs), v in per.items() if GEMM_KERNEL in k and name in v
-                and gs == PREFILL_GEMM_THREADS]
+                and sizes and gs == max(sizes)]
         copy = [v[name] for (d, k, gs), v in per.items() if COPY_KERNEL_HINT in k.lower() and name in v
                 and v[name] * 1024 > CALIB_BYTES * 0.5]
         if not gemm or not copy:
@@ -135,20 +135,27 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
     print("\n".join(lines))
 
 
-def summarize_trace(stats_csv, out_path, command):
-    """Write the per-kernel duration summary of a rocprofv3 --kernel-trace --stats run."""
+def summarize_trace(trace_csv, out_path, command):
+    """Write per-kernel, per-grid-size durations from a rocprofv3
+    --kernel-trace run (its *_kernel_trace.csv): one line per distinct
+    (kernel, grid size), so launches of one kernel at different shapes are
+    not averaged together."""
     import csv
-    rows = list(csv.DictReader(open(stats_csv)))
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            grid = "x".join(r.get(k, "") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z")) \
+                if "Grid_Size_X" in r else r.get("Grid_Size", "")
+            key = (r["Kernel_Name"], grid)
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(dur)
     lines = [f"# rocprofv3 kernel-trace summary: decode/FFN step, MI355X",
              f"# command: {command}",
              f"kernel_source_hash: {kernel_source_hash()}",
-             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
-    for r in rows:
-        name = r["Name"]
-        if len(name) > 110:
-            name = name[:107] + "..."
-        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} {float(r['MinNs'])/1e3:10.2f} "
-                     f"{float(r['MaxNs'])/1e3:10.2f}  {name}")
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  {'grid':>16}  kernel"]
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        short = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"{len(d):6d} {sum(d)/len(d):10.2f} {min(d):10.2f} {max(d):10.2f}  {grid:>16}  {short}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -165,8 +172,8 @@ def main():
                     help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (no GPU needed)")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT"),
-                    help="summarise a rocprofv3 --kernel-trace --stats run (no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "OUT"),
+                    help="summarise a rocprofv3 --kernel-trace run, its *_kernel_trace.csv (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_counters:

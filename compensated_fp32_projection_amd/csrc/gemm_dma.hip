@@ -1,18 +1,32 @@
 // Dual-product MFMA GEMM, main variant: operands go from HBM straight into
-// LDS (buffer_load ... lds), through a four-stage ring.
+// LDS (buffer_load ... lds) through a four-stage ring, and two waves per SIMD
+// take turns on the matrix unit ("ping-pong").
 //
 // Same arithmetic as the generic kernel in gemm.hip (C_hi = A_hi W and
 // C_lo = A_lo W with FP32 accumulators, y = C_hi + C_lo / 1024 merged once in
 // the epilogue; laya.cpp Vulkan guide, compensated-FP32 paragraph), organised
 // for gfx950:
-//   * 256 threads, a 128 x 256 output tile (256 x 256 with the hi and lo rows),
-//     each wave 64 x 128 of both products: 256 FP32 accumulators per lane.
+//   * 512 threads (8 waves, 2 per SIMD), a 128 x 256 output tile (256 x 256
+//     with the hi and lo rows).  Each wave owns 64 rows x 64 columns of both
+//     products: 2 x 2 blocks of v_mfma_f32_32x32x16_f16 per product, 128
+//     FP32 accumulators per lane.  Every W fragment feeds a hi and a lo MFMA.
 //   * K in stages of 32.  Each stage (A_hi, A_lo: 128 x 32 FP16; W: 32 x 256
-//     FP16; 32 KiB) is fetched by 32 wave-wide 1 KiB LDS-DMA loads that need
-//     no registers, so three stages are in flight while a fourth is used.
-//     A wave waits for its own loads of the next stage (vmcnt), then a bare
-//     s_barrier publishes every wave's loads; the ring buffers are separate
-//     LDS objects so the compiler can tell the DMA targets from the reads.
+//     FP16; 32 KiB) is fetched by 32 wave-wide 1 KiB LDS-DMA loads (4 per
+//     wave) that need no registers; three stages are in flight.
+//   * Waves 0-3 and waves 4-7 form two groups, one wave of each per SIMD.  A
+//     wave alternates a memory phase (issue its loads of stage s+3, read its
+//     fragments of stage s from LDS, wait for them) and a compute phase (the
+//     16 MFMAs of stage s at raised priority), with a block barrier after
+//     each.  The second group starts one barrier late, so while one group
+//     multiplies the other loads: each SIMD's matrix unit is fed by one wave
+//     while its partner waits on memory.
+//   * Synchronisation: at the end of its memory phase a wave waits until its
+//     fragment reads have landed and only its loads of the two newest stages
+//     are pending (vmcnt 8).  The barrier that follows therefore publishes
+//     stage s+1 to the group about to read it, and every wave's reads of a
+//     ring buffer complete before the barrier after which it is refilled.
+//     The ring buffers are separate LDS objects, so the compiler can tell the
+//     DMA targets from the reads and inserts no waits of its own.
 //   * A sits in LDS as 16-byte k-granules, row-major, the granule order of
 //     each row XOR-ed with bits of the row index; an MFMA A fragment is one
 //     conflict-free ds_read_b128.  W sits N-contiguous (as in memory), the
@@ -21,7 +35,8 @@
 //     the gfx950 LDS transpose read: in each 16-lane group, lane j's element
 //     e comes from element j%4 of the 8 bytes addressed by lane j/4 + 4e.
 //   * Loads outside the matrices get an offset no buffer reaches and read as
-//     zero, so partial tiles need no branches.
+//     zero, so partial tiles need no branches; stages past the end are loaded
+//     the same way, which keeps every wait count constant.
 #include <type_traits>
 
 #include "device_common.h"
@@ -35,18 +50,24 @@ namespace cfp32 {
 namespace {
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kT = 256;
+constexpr int kT = 512;                             // 8 waves
 constexpr int BM = 128, BN = 256, BK = 32, NST = 4;
+constexpr int WTM = 64, WTN = 64;                   // wave tile (rows per product x columns)
+constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 MFMA blocks per wave and product
+constexpr int WAVES_N = BN / WTN;                   // 4 waves across N, 2 across M
 constexpr int KG = BK / 8;                          // k-granules per A row per stage
-constexpr int A_SLOTS = BM * KG;                    // granules per A plane per stage
-constexpr int WG = BN / 8;                          // granules per W row
-constexpr int W_SLOTS = BK * WG;                    // granules of W per stage
+constexpr int A_SLOTS = BM * KG;                    // granules per A plane per stage (512)
+constexpr int WG = BN / 8;                          // granules per W row (32)
+constexpr int W_SLOTS = BK * WG;                    // granules of W per stage (1024)
 constexpr int STAGE_SLOTS = 2 * A_SLOTS + W_SLOTS;  // 2048 granules = 32 KiB
+constexpr int LOADS_PER_WAVE = 4;                   // 1 per A plane + 2 for W
 constexpr int kNoOffset = 0x7FFFFFF0;
 constexpr int kBufferWord3 = 0x00020000;
 
-static_assert(A_SLOTS % (64 * 4) == 0 && W_SLOTS % (64 * 4) == 0, "DMA loads split evenly over 4 waves");
+static_assert(A_SLOTS == 64 * (kT / 64) && W_SLOTS == 2 * 64 * (kT / 64), "each wave loads 1 A granule row per plane and 2 of W");
+static_assert((BM / WTM) * WAVES_N == kT / 64, "wave tiles cover the block tile");
 
 __shared__ uint4 g_stage0[STAGE_SLOTS];
 __shared__ uint4 g_stage1[STAGE_SLOTS];
@@ -72,13 +93,9 @@ __device__ __forceinline__ int w_slot(int k, int ng)
     return 2 * A_SLOTS + k * WG + (ng ^ ((k & 3) << 2));
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
+// s_waitcnt immediates (gfx9 encoding): vector-memory count N, LDS count 0 or any.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 __device__ __forceinline__ void block_barrier()
 {
@@ -106,9 +123,10 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: barriers branch on it
+    const int group = wave >> 2;                                 // waves 0-3 and 4-7; one of each per SIMD
+    const int wm = wave / WAVES_N;
+    const int wn = wave % WAVES_N;
 
     const int64_t nbm = (g.M + BM - 1) / BM;
     const int64_t nbn = (g.N + BN - 1) / BN;
@@ -124,23 +142,22 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const __amdgpu_buffer_rsrc_t rs_w =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
 
-    // Which granule this lane fetches in each of its DMA loads.  Load j of a
-    // plane fills slots 64j .. 64j+63; lane i fills slot 64j + i.  The byte
-    // offsets of stage 0 are formed once; a stage adds 2*k0 (A) or
-    // 2*k0*ldw (W).  Granules outside the operands use kNoOffset.
-    int a_off[2], a_kend[2], w_off[4], w_kend[4];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int slot = 64 * (2 * wave + jj) + lane;
+    // This wave's loads of a stage: granules 64*wave + lane of each A plane
+    // and 64*(2*wave + jj) + lane of W (lane i fills slot base + i).  Byte
+    // offsets of stage 0 are formed once; a stage adds 2*k0 (A) or 2*k0*ldw
+    // (W).  Granules outside the operands use kNoOffset.
+    int a_off, a_kend, w_off[2], w_kend[2];
+    {
+        const int slot = 64 * wave + lane;
         const int row = slot / KG;
         const int kg = (slot % KG) ^ ((row >> 2) & 3);
         const bool ok = m0 + row < g.M;
-        a_off[jj] = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
-        a_kend[jj] = ok ? (int)(g.Ka - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
+        a_off = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
+        a_kend = ok ? (int)(g.Ka - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
     }
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int slot = 64 * (4 * wave + jj) + lane;
+    for (int jj = 0; jj < 2; ++jj) {
+        const int slot = 64 * (2 * wave + jj) + lane;
         const int k = slot / WG;
         const int ng = (slot % WG) ^ ((k & 3) << 2);
         const bool ok = n0 + 8 * ng < g.N;
@@ -152,148 +169,113 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         constexpr int S = decltype(stage_tag)::value;
         uint4 *s = stage_buf<S>();
         const int k0 = (int)k0_64;
+        const int a = k0 < a_kend ? a_off + 2 * k0 : kNoOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0, 0);
         const int wstep = (int)(k0_64 * g.ldw * 2);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * wave + jj;
-            const int off = k0 < a_kend[jj] ? a_off[jj] + 2 * k0 : kNoOffset;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * j), 16, off, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * j), 16, off, 0, 0, 0);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int j = 4 * wave + jj;
-            const int off = k0 < w_kend[jj] ? w_off[jj] + wstep : kNoOffset;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(s + 2 * A_SLOTS + 64 * j), 16, off, 0, 0, 0);
+            const int o = k0 < w_kend[jj] ? w_off[jj] + wstep : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(s + 2 * A_SLOTS + 64 * (2 * wave + jj)),
+                                                     16, o, 0, 0, 0);
         }
     };
 
-    floatx16_t acc_hi[2][4], acc_lo[2][4];
+    floatx16_t acc_hi[TM][TN], acc_lo[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc_hi[i][j] = floatx16_t{}, acc_lo[i][j] = floatx16_t{};
+        for (int j = 0; j < TN; ++j) acc_hi[i][j] = floatx16_t{}, acc_lo[i][j] = floatx16_t{};
 
     struct Frags {
-        half8_t ah[2], al[2], bw[4];
+        half8_t ah[TM], al[TM], bw[TN];
     };
     // Per-lane parts of the fragment addresses.
-    const int a_row0 = wm * 64 + (lane & 31);
+    const int a_row0 = wm * WTM + (lane & 31);
     const int b_kl = 8 * (lane >> 5) + ((lane & 15) >> 2);                 // + 16 ks + 4 h
-    const int b_n0 = wn * 128 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 tn
+    const int b_n0 = wn * WTN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 j
 
     auto read_frags = [&](const uint4 *s, int ks, Frags &f) {
         const int kg = 2 * ks + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < TM; ++i) {
             const int row = a_row0 + 32 * i;
             f.ah[i] = __builtin_bit_cast(half8_t, s[a_slot(0, row, kg)]);
             f.al[i] = __builtin_bit_cast(half8_t, s[a_slot(1, row, kg)]);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TN; ++j) {
             const int n = b_n0 + 32 * j;
             short4_t t[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int k = 16 * ks + 4 * h + b_kl;
                 const int byte = w_slot(k, n >> 3) * 16 + (n & 7) * 2;
-                t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (CFP32_LDS short4_t *)((CFP32_LDS char *)s + byte));
+                t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CFP32_LDS short4_t *)((CFP32_LDS char *)s + byte));
             }
-            typedef short short8_t __attribute__((ext_vector_type(8)));
             const short8_t v = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
             f.bw[j] = __builtin_bit_cast(half8_t, v);
         }
     };
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TN; ++j) {
                 acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
                 acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
             }
     };
 
     const int64_t nk = (g.Ka + BK - 1) / BK;
-
-    // Software pipeline over K stages (ring of NST = 4 LDS buffers).
-    // Invariant at the top of step s: the fragments of stage s are in
-    // registers (set F), the loads of stages s+1, s+2, s+3 are in flight
-    // (8 per wave each), and buffer s&3 is free once every wave's reads of
-    // it have completed.  Step s:
-    //   1. wait until this wave's reads are done (lgkmcnt 0) and 16 loads
-    //      remain (stage s+1 landed), then a barrier: stage s+1 is complete
-    //      for every wave and nobody reads buffer s&3 any more;
-    //   2. refill buffer s&3 with stage s+4;
-    //   3. read stage s+1's fragments into the other register set;
-    //   4. run stage s's 32 MFMAs, which overlap step 3's LDS reads.
-    // Stages past the end are issued too: all their offsets fall outside the
-    // operands, so they read zeros into a buffer nobody reads, and the wait
-    // count stays one constant.
-    auto read_stage = [&](const uint4 *buf, Frags (&f)[2]) {
-        read_frags(buf, 0, f[0]);
-        read_frags(buf, 1, f[1]);
-    };
-    auto step = [&](auto stage_tag, int64_t s, Frags (&cur)[2], Frags (&nxt)[2]) {
+    Frags f0, f1;
+    // One stage for this wave: memory phase, barrier, compute phase, barrier.
+    auto stage = [&](auto stage_tag, int64_t s) {
         constexpr int S = decltype(stage_tag)::value;
-        __builtin_amdgcn_s_waitcnt((16 & 15) | (1 << 14) | (7 << 4) | (0 << 8));  // vmcnt(16) lgkmcnt(0)
+        issue(std::integral_constant<int, (S + 3) & 3>{}, (s + 3) * BK);
+        const uint4 *buf = stage_buf<S>();
+        read_frags(buf, 0, f0);
+        read_frags(buf, 1, f1);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
         block_barrier();
-        issue(std::integral_constant<int, S>{}, (s + 4) * BK);
-        read_stage(stage_buf<(S + 1) & 3>(), nxt);
-        mfmas(cur[0]);
-        mfmas(cur[1]);
-        // Instruction order for the scheduler: the 8 DMA loads and 24 LDS
-        // reads of this step are threaded between the first 16 of its 32
-        // MFMAs (MFMA, load, 2 reads; then MFMA, read), so the matrix pipe is
-        // fed while they issue instead of idling behind a block of them.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (the DMA)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_s_setprio(1);
+        mfmas(f0);
+        mfmas(f1);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
     };
 
-    Frags fa[2], fb[2];
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, BK);
     issue(std::integral_constant<int, 2>{}, 2 * BK);
-    issue(std::integral_constant<int, 3>{}, 3 * BK);
-    wait_vmcnt<24>();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS_PER_WAVE));  // stage 0 landed for this wave
     block_barrier();
-    read_stage(stage_buf<0>(), fa);
+    if (group == 1) block_barrier();  // the second group runs one phase behind
     const int64_t nk4 = nk / NST * NST;
     for (int64_t s0 = 0; s0 < nk4; s0 += NST) {
-        step(std::integral_constant<int, 0>{}, s0, fa, fb);
-        step(std::integral_constant<int, 1>{}, s0 + 1, fb, fa);
-        step(std::integral_constant<int, 2>{}, s0 + 2, fa, fb);
-        step(std::integral_constant<int, 3>{}, s0 + 3, fb, fa);
+        stage(std::integral_constant<int, 0>{}, s0);
+        stage(std::integral_constant<int, 1>{}, s0 + 1);
+        stage(std::integral_constant<int, 2>{}, s0 + 2);
+        stage(std::integral_constant<int, 3>{}, s0 + 3);
     }
-    if (nk4 < nk) step(std::integral_constant<int, 0>{}, nk4, fa, fb);
-    if (nk4 + 1 < nk) step(std::integral_constant<int, 1>{}, nk4 + 1, fb, fa);
-    if (nk4 + 2 < nk) step(std::integral_constant<int, 2>{}, nk4 + 2, fa, fb);
-    wait_vmcnt<0>();  // drain the trailing zero loads before the block exits
+    if (nk4 < nk) stage(std::integral_constant<int, 0>{}, nk4);
+    if (nk4 + 1 < nk) stage(std::integral_constant<int, 1>{}, nk4 + 1);
+    if (nk4 + 2 < nk) stage(std::integral_constant<int, 2>{}, nk4 + 2);
+    if (group == 0) block_barrier();  // both groups pass the same number of barriers
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the trailing zero loads before the block exits
 
     // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31);
     // element e holds row 8*(e/4) + 4*(lane/32) + (e%4) of the block.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+        for (int j = 0; j < TN; ++j) {
+            const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
             if (col >= g.N) continue;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (row >= g.M) continue;
                 const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
                 // Outputs are written once: non-temporal stores keep them from

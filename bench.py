@@ -209,6 +209,8 @@ def main():
     x2 = torch.from_numpy(A2).to(dev)
     y1 = torch.empty((M_DEC, N_), dtype=torch.float32, device=dev)
     y2 = torch.empty((M_PRE, N_), dtype=torch.float32, device=dev)
+    dec_ws_bytes = cf.cfp32_linear_workspace_bytes(M_DEC, N_, K_)
+    dec_ws = torch.empty(max(dec_ws_bytes, 1), dtype=torch.uint8, device=dev)
     hi = torch.empty((M_PRE, K_), dtype=torch.int16, device=dev)
     lo = torch.empty((M_PRE, K_), dtype=torch.int16, device=dev)
 
@@ -219,7 +221,8 @@ def main():
     def step(s, ev=None):
         w = Ws[s % len(Ws)].data_ptr()
         if ev: ev[0].record(stream)
-        check(cf.cfp32_linear(x1.data_ptr(), K_, w, N_, y1.data_ptr(), N_, M_DEC, N_, K_, None, 0, sh), "decode")
+        check(cf.cfp32_linear(x1.data_ptr(), K_, w, N_, y1.data_ptr(), N_, M_DEC, N_, K_,
+                              dec_ws.data_ptr(), dec_ws_bytes, sh), "decode")
         if ev: ev[1].record(stream)
         check(cf.cfp32_split(x2.data_ptr(), K_, hi.data_ptr(), lo.data_ptr(), K_, M_PRE, K_, sh), "split")
         if ev: ev[2].record(stream)
@@ -265,7 +268,7 @@ def main():
         return a.elapsed_time(b) / n * 1e3
 
     gemv_us = timed(lambda i: check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y1.data_ptr(), N_,
-                                                    M_DEC, N_, K_, None, 0, sh), "decode"), 100)
+                                                    M_DEC, N_, K_, dec_ws.data_ptr(), dec_ws_bytes, sh), "decode"), 100)
     sq = workloads.square()
     xs = torch.from_numpy(sq.A[0]).to(dev)
     ws = torch.from_numpy(sq.W.view(np.int16)).to(dev)

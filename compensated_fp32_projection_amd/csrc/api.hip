@@ -61,9 +61,10 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout for M > 8: the hi plane, then the lo plane, each
-// [M, ldh] FP16 with ldh = K rounded up to 8 (16-byte rows), each starting
-// on a 256-byte boundary of the (realigned) workspace pointer.
+// Workspace layout, from the caller's pointer rounded up to 256 bytes.
+// M > 8: the hi plane, then the lo plane, each [M, ldh] FP16 with ldh = K
+// rounded up to 8 (16-byte rows), each starting on a 256-byte boundary.
+// M <= 8: the FP32 per-chunk partial sums of the small-M path (GemvPlan).
 int64_t split_ld(int64_t K) { return (K + 7) / 8 * 8; }
 
 size_t plane_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)split_ld(K) * 2u, kAlign); }
@@ -131,9 +132,14 @@ cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (!dims_ok(M, N) || !dims_ok(K, 0)) return 0;
-    if (M <= cfp32::kGemvMaxRows || N == 0 || K == 0) return 0;
+    if (M == 0 || N == 0 || K == 0) return 0;
+    // + kAlign: slack to realign the caller's pointer.
+    if (M <= cfp32::kGemvMaxRows) {
+        const size_t b = cfp32::gemv_plan(M, N, K).workspace_bytes;
+        return b == 0 ? 0 : b + kAlign;
+    }
     if (!extent_ok(M, split_ld(K))) return 0;
-    return 2 * plane_bytes(M, K) + kAlign;  // + slack to realign the caller's pointer
+    return 2 * plane_bytes(M, K) + kAlign;
 }
 
 cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
@@ -153,13 +159,17 @@ cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_
     if (st != CFP32_OK) return st;
     hipStream_t s = (hipStream_t)stream;
 
-    if (M <= cfp32::kGemvMaxRows) return launched(cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, s));
+    const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
+    if (M <= cfp32::kGemvMaxRows) {
+        // need == 0: K == 0, or K is one chunk and the product kernel merges itself.
+        float *part = need > 0 ? reinterpret_cast<float *>(base) : nullptr;
+        return launched(cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, part, need > 0 ? need - kAlign : 0, s));
+    }
 
     if (K == 0)  // nothing to split: the product of an empty sum is +0
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s));
 
-    const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);
     uint16_t *lo = reinterpret_cast<uint16_t *>(base + plane_bytes(M, K));
     const int64_t ldh = split_ld(K);

@@ -1,60 +1,337 @@
-// Fused projection for 1 <= M <= 8 rows (decode-sized inputs).
+// Small-M projection (1 <= M <= 8 rows, decode-sized inputs).
 //
 // The laya.cpp Vulkan guide runs small projections at their real batch size,
 // with no padding of the row count.  At M <= 8 the projection streams W once
-// and does almost no arithmetic per byte, so it is bound by HBM bandwidth and
-// by launch latency: one kernel does the split, both products and the merge.
+// and does little arithmetic per byte, so it is bound by HBM bandwidth; W is
+// read in whole 1 KiB row segments (512 columns), the access pattern that
+// streams fastest, and K is cut into row chunks so that there are enough
+// blocks to keep every CU loading.
 //
-// gfx950 design
-//   * A block owns NB consecutive output columns and all of K.  Its threads
-//     form CH = NB/8 column groups (8 FP16 columns = one 16-byte load) times
-//     KL = THREADS/CH k-lanes; k-lane kl handles rows kl, kl+KL, kl+2KL, ...
-//     A wave reads 64/CH rows x 16*CH contiguous bytes per load instruction.
-//   * U loads per thread are issued before any of them is used, to keep
-//     enough bytes in flight per CU to cover HBM latency.
-//   * x is split in registers (same split as the standalone kernel); both
-//     products accumulate in FP32 with fused multiply-adds (an FP16 x FP16
-//     product is exact in FP32, so fusing does not change any rounding).
-//   * The k-lane partial sums are reduced in a fixed order -- a butterfly
-//     inside each wave, then the waves in index order through LDS -- so
-//     results are identical from run to run; the merge follows, once per
-//     output, after both reductions are complete.
+// Two dispatches, as in the guide's description of the method (the products,
+// then the merge as one dispatch):
+//
+//  1. gemv_mfma_kernel -- split + both products.  A block (4 waves) owns one
+//     512-column tile of one row chunk and walks it in stages of 32 rows
+//     through a four-buffer LDS ring filled by LDS-DMA loads (W: one 1 KiB
+//     row per wave instruction, streaming cache policy; x: the chunk's 32
+//     columns of every row, 4 bytes per lane, so x needs no alignment).
+//     The matrix unit does the products: the hi and lo halves of the M rows
+//     are interleaved into the 16 rows of one v_mfma_f32_16x16x32_f16 A
+//     operand (row 2m = hi of x row m, row 2m + 1 = lo), so one MFMA chain
+//     forms C_hi and C_lo together with FP32 accumulators, and the split of
+//     x happens in registers as the A fragment is built.  Each wave owns 128
+//     columns (8 MFMA tiles); no reduction across waves is needed.  The block
+//     writes its chunk's C_hi and C_lo partial sums to the workspace, or, when
+//     K is a single chunk, merges and writes y itself (no second dispatch).
+//  2. gemv_merge_kernel -- for every output, sums the chunk partials of C_hi
+//     and of C_lo in chunk order, then merges y = C_hi + C_lo / 1024.
+//
+// Every summation order is fixed, so results are identical from run to run.
+// W that is not 16-byte aligned with ldw % 8 == 0 (or too large for 32-bit
+// buffer offsets) goes through gemv_generic_kernel instead: one launch, a
+// block per 64 columns and all of K, element loads, FP32 FMAs on the vector
+// unit (an FP16 x FP16 product is exact in FP32, so fusing it into the
+// accumulation rounds once, as the matrix unit does).
+#include <climits>
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
+
+#define CFP32_LDS __attribute__((address_space(3)))
 
 namespace cfp32 {
 
 namespace {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
 constexpr int kNoOffset = 0x7FFFFFF0;      // a raw buffer load here reads zero
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 constexpr int kStreamAux = 2;             // cache policy "nt": W is read once, do not keep it in cache
+constexpr int kTileN = 512;               // columns per tile: 1 KiB of an FP16 row
+constexpr int kTargetBlocks = 256;        // one block per CU
+constexpr int kT = 256;                   // 4 waves, 128 columns each
+constexpr int kBK = 32;                   // rows of W per stage (the MFMA's k)
+constexpr int kRowSlots = kTileN / 8;     // 16-byte granules per W row in LDS
+constexpr int kWSlots = kBK * kRowSlots;  // 2048 granules: 32 KiB of W per stage
+constexpr int kXSlots = 64;               // 1 KiB: x[8 rows][32 columns] FP32 per stage
+constexpr int kLoadsPerStage = kBK / (kT / 64) + 1;  // per wave: 8 W rows + 1 x load
 
-// THREADS threads own NB output columns; U loads per thread in flight.
-// BUF: W is 16-byte aligned with ldw % 8 == 0 and under 2^31 bytes, so W is
-// read with raw buffer loads whose out-of-range lanes read zero (no branches,
-// so all U loads of a thread are in flight together); otherwise W is read
-// through the guarded element path.
-template <int MR, bool BUF, int THREADS, int NB, int U>
-__global__ __launch_bounds__(THREADS) void gemv_kernel(const float *__restrict__ x, int64_t ldx,
-                                                       const uint16_t *__restrict__ w, int64_t ldw,
-                                                       float *__restrict__ y, int64_t ldy, int64_t N, int64_t K)
+// Separate LDS objects per ring buffer (and for W and x), so that the
+// compiler can tell which DMA fills which buffer and adds no waits of its own.
+__shared__ uint4 g_wring0[kWSlots];
+__shared__ uint4 g_wring1[kWSlots];
+__shared__ uint4 g_wring2[kWSlots];
+__shared__ uint4 g_wring3[kWSlots];
+__shared__ uint4 g_xring0[kXSlots];
+__shared__ uint4 g_xring1[kXSlots];
+__shared__ uint4 g_xring2[kXSlots];
+__shared__ uint4 g_xring3[kXSlots];
+
+template <int B>
+__device__ __forceinline__ uint4 *wring()
 {
-    constexpr int CH = NB / 8;
-    constexpr int KL = THREADS / CH;
-    constexpr int WAVES = THREADS / 64;
-    static_assert(CH <= 64 && (CH & (CH - 1)) == 0, "column groups are a power of two within a wave");
+    if constexpr (B == 0) return g_wring0;
+    else if constexpr (B == 1) return g_wring1;
+    else if constexpr (B == 2) return g_wring2;
+    else return g_wring3;
+}
 
+template <int B>
+__device__ __forceinline__ uint4 *xring()
+{
+    if constexpr (B == 0) return g_xring0;
+    else if constexpr (B == 1) return g_xring1;
+    else if constexpr (B == 2) return g_xring2;
+    else return g_xring3;
+}
+
+// W row r of a stage sits in granules [64 r, 64 r + 64); its column granule c
+// (columns 8c .. 8c + 7) is stored at position c ^ 2 (r % 4), so the four
+// rows that one transposed read touches fall on different banks.
+__device__ __forceinline__ int w_slot(int r, int c) { return r * kRowSlots + (c ^ ((r & 3) << 1)); }
+
+// s_waitcnt immediates (gfx9 encoding): vector-memory count n, LDS count 0.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct GemvArgs {
+    const float *x;
+    int64_t ldx;
+    const uint16_t *w;
+    int64_t ldw;
+    float *part;      // [chunks][M][2][n_pad] partial sums (chunks > 1)
+    float *y;         // written directly when chunks == 1
+    int64_t ldy;
+    int64_t n_pad;
+    int64_t M, N, K;
+    int64_t stages;   // ceil(K / 32)
+    int64_t chunks;   // the stages split as evenly as possible, in order
+    int64_t ntiles;   // ceil(N / 512)
+};
+
+__global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Chunk c holds `base` stages, plus one for the first `extra` chunks.
+    const unsigned ntiles = (unsigned)g.ntiles;
+    const int tile = (int)(blockIdx.x % ntiles);
+    const int chunk = (int)(blockIdx.x / ntiles);
+    const int base = (int)(g.stages / g.chunks);
+    const int extra = (int)(g.stages % g.chunks);
+    const int s_begin = chunk * base + (chunk < extra ? chunk : extra);
+    const int ns = base + (chunk < extra ? 1 : 0);  // >= 1: chunks <= stages
+    const int64_t s_end = s_begin + ns;
+    const int64_t r0 = (int64_t)kBK * s_begin;
+    const int64_t n0 = tile * kTileN;
+    const int M = (int)g.M;
+
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g.x), 0, (int)(g.M * g.ldx * 4), kBufferWord3);
+
+    // DMA sources of this lane.  W: the wave loads rows 8 wave + j of a stage,
+    // lane l the granule that belongs at position l of that row.  x: the wave
+    // loads rows 2 wave and 2 wave + 1, lane l column l % 32.  A load whose
+    // row lies past the chunk (or past K), or whose column lies past N, gets
+    // an offset no buffer reaches and writes zeros; each limit below is the
+    // first stage row offset k0 at which that happens.
+    const int k_limit = (int)(kBK * s_end < g.K ? kBK * s_end : g.K);
+    const unsigned ldw2 = (unsigned)(g.ldw * 2);
+    int w_col[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = lane ^ (q << 1);  // rows with r % 4 == q
+        w_col[q] = n0 + 8 * c < g.N ? (int)((n0 + 8 * c) * 2) : -1;
+    }
+    int w_kend[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w_kend[j] = w_col[j & 3] >= 0 ? k_limit - (8 * wave + j) : INT_MIN;
+    const int xm = 2 * wave + (lane >> 5);
+    const int xk = lane & 31;
+    const int x_kend = xm < M ? k_limit - xk : INT_MIN;
+    const int x_off = xm < M ? (int)((xm * g.ldx + xk) * 4) : 0;
+
+    auto issue = [&](auto buf_tag, int s) {
+        constexpr int B = decltype(buf_tag)::value;
+        uint4 *buf = wring<B>();
+        const int k0 = (int)r0 + kBK * s;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * wave + j;
+            const int o = k0 < w_kend[j] ? w_col[j & 3] + (int)((unsigned)(k0 + r) * ldw2) : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(buf + r * kRowSlots), 16, o, 0, 0,
+                                                     kStreamAux);
+        }
+        const int ox = k0 < x_kend ? x_off + 4 * k0 : kNoOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(xring<B>() + 16 * wave), 4, ox, 0, 0, 0);
+    };
+
+    // Fragment addresses.  A: lane l is row i = l % 16 (x row i / 2, hi for
+    // even i, lo for odd i) and k = 8 (l / 16) + e.  B (two transposed reads
+    // of 4 rows each): lane l's column is 128 wave + 16 t + l % 16.
+    const int ai = lane & 15;
+    const int am = ai >> 1;
+    const bool a_live = am < M;
+    const bool a_lo = ai & 1;
+    const int kq = lane >> 4;
+    const int j4 = (lane & 15) >> 2;
+    const int b_row = 8 * kq + j4;                  // + 4 h
+    const int b_col = 16 * wave + ((lane & 3) >> 1);  // granule, + 2 t
+    const int b_half = (lane & 1) * 8;                // byte within the granule
+
+    floatx4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = floatx4_t{};
+
+    auto compute = [&](const uint4 *buf, const uint4 *xb) {
+        // x[am][8 kq .. 8 kq + 7] (rows of 32 floats = 8 granules).
+        const floatx4_t x0 = __builtin_bit_cast(floatx4_t, xb[am * 8 + 2 * kq]);
+        const floatx4_t x1 = __builtin_bit_cast(floatx4_t, xb[am * 8 + 2 * kq + 1]);
+        half8_t a;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            _Float16 h, l;
+            split_value(e < 4 ? x0[e] : x1[e - 4], h, l);
+            a[e] = a_live ? (a_lo ? l : h) : (_Float16)0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            short4_t v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int r = b_row + 4 * h;
+                const int byte = w_slot(r, b_col + 2 * t) * 16 + b_half;
+                v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CFP32_LDS short4_t *)((CFP32_LDS char *)buf + byte));
+            }
+            const short8_t b = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, b), acc[t], 0, 0, 0);
+        }
+    };
+
+    // One stage: refill the buffer read one stage ago with stage s + 3, use
+    // stage s, then wait until stage s + 1 has landed (two stages may stay in
+    // flight) and this wave's LDS reads are done; the barrier publishes stage
+    // s + 1 and frees stage s's buffer for the next refill.
+    auto stage = [&](auto buf_tag, int s) {
+        constexpr int B = decltype(buf_tag)::value;
+        issue(std::integral_constant<int, (B + 3) & 3>{}, s + 3);
+        compute(wring<B>(), xring<B>());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kLoadsPerStage));
+        block_barrier();
+    };
+
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 2>{}, 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoadsPerStage));  // stage 0 landed for this wave
+    block_barrier();
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+        stage(std::integral_constant<int, 0>{}, s);
+        stage(std::integral_constant<int, 1>{}, s + 1);
+        stage(std::integral_constant<int, 2>{}, s + 2);
+        stage(std::integral_constant<int, 3>{}, s + 3);
+    }
+    if (s < ns) stage(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < ns) stage(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 2 < ns) stage(std::integral_constant<int, 2>{}, s + 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero loads land before the block exits
+
+    // 16x16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + e.
+    // Rows 4 (l / 16) + 0, 1 are hi, lo of x row 2 (l / 16); + 2, 3 of the next.
+    const int64_t col0 = n0 + 128 * wave + (lane & 15);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int m = 2 * kq + q;
+        if (m >= M) continue;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int64_t n = col0 + 16 * t;
+            const float ch = acc[t][2 * q], cl = acc[t][2 * q + 1];
+            if (g.chunks == 1) {
+                if (n < g.N) __builtin_nontemporal_store(merge_value(ch, cl), g.y + m * g.ldy + n);
+            } else {
+                // Streaming stores: the merge dispatch reads these from
+                // memory anyway (they come from every XCD).
+                float *p = g.part + ((chunk * g.M + m) * 2) * g.n_pad + n;
+                __builtin_nontemporal_store(ch, p);
+                __builtin_nontemporal_store(cl, p + g.n_pad);
+            }
+        }
+    }
+}
+
+// y[m, n] = merge(sum over chunks of C_hi, sum over chunks of C_lo), chunks in
+// order.  The partial sums were written by blocks on every XCD, so they come
+// from memory, not from this XCD's L2: all loads of a batch of kMergeBatch
+// chunks are issued before the first add, one memory latency per batch.
+constexpr int kMergeBatch = 16;
+
+__global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict__ part, int64_t n_pad,
+                                                         int64_t chunks, int M, int64_t N,
+                                                         float *__restrict__ y, int64_t ldy)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int m = (int)(i / N);
+    const int64_t n = i % N;
+    const int64_t stride = (int64_t)M * 2 * n_pad;  // from one chunk to the next
+    const float *p = part + (int64_t)m * 2 * n_pad + n;
+    float th = 0.0f, tl = 0.0f;
+    for (int64_t c0 = 0; c0 < chunks; c0 += kMergeBatch) {
+        float vh[kMergeBatch], vl[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            const bool in = c0 + j < chunks;
+            vh[j] = in ? __builtin_nontemporal_load(p + (c0 + j) * stride) : 0.0f;
+            vl[j] = in ? __builtin_nontemporal_load(p + (c0 + j) * stride + n_pad) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; ++j) {
+            if (c0 + j < chunks) {
+                th += vh[j];
+                tl += vl[j];
+            }
+        }
+    }
+    __builtin_nontemporal_store(merge_value(th, tl), y + m * ldy + n);
+}
+
+// Fallback for W that is not 16-byte aligned or too large for 32-bit buffer
+// offsets: a block per 64 columns and all of K, element loads, the same
+// fixed-order reduction inside the block, one launch, no workspace.
+constexpr int kGenericThreads = 512;
+constexpr int kGenericNB = 64;
+
+template <int MR>
+__global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const float *__restrict__ x, int64_t ldx,
+                                                                       const uint16_t *__restrict__ w, int64_t ldw,
+                                                                       float *__restrict__ y, int64_t ldy,
+                                                                       int64_t N, int64_t K)
+{
+    constexpr int CH = kGenericNB / 8;
+    constexpr int KL = kGenericThreads / CH;
+    constexpr int WAVES = kGenericThreads / 64;
     __shared__ float red[WAVES][CH][MR][8][2];
 
     const int tid = threadIdx.x;
     const int c = tid % CH;
     const int kl = tid / CH;
-    const int64_t n0 = (int64_t)blockIdx.x * NB;
+    const int64_t n0 = (int64_t)blockIdx.x * kGenericNB;
     const int64_t n = n0 + 8 * c;
-
-    const __amdgpu_buffer_rsrc_t rs_w =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0, BUF ? (int)(K * ldw * 2) : 0, kBufferWord3);
 
     float sh[MR][8], sl[MR][8];
 #pragma unroll
@@ -62,47 +339,24 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const float *__restrict__
 #pragma unroll
         for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
 
-    for (int64_t kb = kl; kb < K; kb += (int64_t)KL * U) {
-        // x first, then W: the vector-memory counter drains in issue order, so
-        // one wait for the last W load covers every x of the batch.
-        float xv[U][MR];
+    for (int64_t k = kl; k < K; k += KL) {
+        const uint4 wv = load_row8<false>(w + k * ldw, n, N);
+        const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+        float wf[8];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = kb + (int64_t)u * KL;
+        for (int e = 0; e < 8; ++e) wf[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
 #pragma unroll
-            for (int m = 0; m < MR; ++m) xv[u][m] = (k < K) ? x[m * ldx + k] : 0.0f;
-        }
-        uint4 wv[U];
+        for (int m = 0; m < MR; ++m) {
+            _Float16 h16, l16;
+            split_value(x[m * ldx + k], h16, l16);
+            const float h = (float)h16, l = (float)l16;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = kb + (int64_t)u * KL;
-            if constexpr (BUF) {
-                const int off = (k < K && n < N) ? (int)((k * ldw + n) * 2) : kNoOffset;
-                wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, kStreamAux));
-            } else {
-                wv[u] = (k < K) ? load_row8<false>(w + k * ldw, n, N) : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
-            float wf[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) wf[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                _Float16 h16, l16;
-                split_value(xv[u][m], h16, l16);
-                const float h = (float)h16, l = (float)l16;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sh[m][e] = __builtin_fmaf(h, wf[e], sh[m][e]);
-                    sl[m][e] = __builtin_fmaf(l, wf[e], sl[m][e]);
-                }
+            for (int e = 0; e < 8; ++e) {
+                sh[m][e] = __builtin_fmaf(h, wf[e], sh[m][e]);
+                sl[m][e] = __builtin_fmaf(l, wf[e], sl[m][e]);
             }
         }
     }
-
     // Butterfly over the k-lanes of this wave (lanes c, c+CH, c+2CH, ...).
 #pragma unroll
     for (int sft = CH; sft < 64; sft <<= 1)
@@ -124,66 +378,88 @@ __global__ __launch_bounds__(THREADS) void gemv_kernel(const float *__restrict__
             }
     }
     __syncthreads();
-
-    // Waves in index order, then the merge; one thread per output.
-    for (int o = tid; o < MR * NB; o += THREADS) {
-        const int m = o / NB, col = o % NB;
+    for (int o = tid; o < MR * kGenericNB; o += kGenericThreads) {
+        const int m = o / kGenericNB, col = o % kGenericNB;
         const int64_t gn = n0 + col;
         if (gn >= N) continue;
         float th = 0.0f, tl = 0.0f;
 #pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) {
-            th += red[wv][col >> 3][m][col & 7][0];
-            tl += red[wv][col >> 3][m][col & 7][1];
+        for (int v = 0; v < WAVES; ++v) {
+            th += red[v][col >> 3][m][col & 7][0];
+            tl += red[v][col >> 3][m][col & 7][1];
         }
         y[m * ldy + gn] = merge_value(th, tl);
     }
 }
 
-template <int MR, int THREADS, int NB, int U>
-hipError_t launch_cfg(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                      int64_t N, int64_t K, hipStream_t stream)
+int64_t tiles_of(int64_t N) { return (N + kTileN - 1) / kTileN; }
+
+// 32-bit buffer offsets must reach every byte of W and x.
+bool buffer_path_ok(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int64_t M, int64_t K)
 {
-    const int64_t blocks = (N + NB - 1) / NB;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks);
-    const bool buf = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
-                     (K + 1) * ldw * 2 < kNoOffset - (1 << 20);
-    if (buf)
-        gemv_kernel<MR, true, THREADS, NB, U><<<grid, THREADS, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
-    else
-        gemv_kernel<MR, false, THREADS, NB, U><<<grid, THREADS, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
-    return hipGetLastError();
+    constexpr int64_t kLimit = kNoOffset - (1 << 20);
+    return (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0) &&
+           ((reinterpret_cast<uintptr_t>(x) & 3) == 0) && (K + 1) * ldw * 2 < kLimit && M * ldx * 4 < kLimit;
 }
 
-// Launch shape per row count: 1024 threads keep more loads in flight while
-// the accumulators are few; from three rows on, 512 threads leave each
-// thread enough registers for 2 x 8 x M accumulators.
 template <int MR>
-hipError_t launch_rows(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                       int64_t N, int64_t K, hipStream_t stream)
+hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                          int64_t N, int64_t K, hipStream_t stream)
 {
-    if constexpr (MR <= 2)
-        return launch_cfg<MR, 1024, 64, 8>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    else
-        return launch_cfg<MR, 512, 64, 8>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    const int64_t blocks = (N + kGenericNB - 1) / kGenericNB;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    gemv_generic_kernel<MR><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream)
+// About one block per CU over all column tiles; a chunk has at least one
+// stage of 32 rows.
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
 {
+    GemvPlan p{};
+    if (M <= 0 || M > kGemvMaxRows || N <= 0 || K <= 0) return p;
+    const int64_t ntiles = tiles_of(N);
+    if (ntiles > ((int64_t)1 << 40)) return p;  // keeps the byte count below in range
+    p.stages = (K + kBK - 1) / kBK;
+    int64_t chunks = kTargetBlocks / ntiles;
+    if (chunks > p.stages) chunks = p.stages;
+    if (chunks < 1) chunks = 1;
+    p.chunks = chunks;
+    p.n_pad = ntiles * kTileN;
+    p.workspace_bytes = chunks == 1 ? 0 : (size_t)chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                       int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream)
+{
+    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    const GemvPlan p = gemv_plan(M, N, K);
+    if (p.chunks > 0 && buffer_path_ok(x, ldx, w, ldw, M, K) &&
+        (p.workspace_bytes == 0 || (part && part_bytes >= p.workspace_bytes))) {
+        const int64_t blocks = tiles_of(N) * p.chunks;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N)};
+        gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || p.chunks == 1) return e;
+        const int64_t outs = M * N;
+        if ((outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks, (int)M,
+                                                                                     N, y, ldy);
+        return hipGetLastError();
+    }
     switch (M) {
-    case 1: return launch_rows<1>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 2: return launch_rows<2>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 3: return launch_rows<3>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 4: return launch_rows<4>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 5: return launch_rows<5>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 6: return launch_rows<6>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 7: return launch_rows<7>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 8: return launch_rows<8>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    default: return hipErrorInvalidValue;
+    case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 3: return launch_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 4: return launch_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 5: return launch_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 6: return launch_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 7: return launch_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    default: return launch_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream);
     }
 }
 

@@ -28,10 +28,28 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                            int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
 
-// Fused split + both products + merge for 1 <= M <= 8.
-hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
-                       int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
-
 constexpr int64_t kGemvMaxRows = 8;
+
+// Small-M (1 <= M <= 8) path: K is cut into `chunks` row chunks of whole
+// stages (`stages` = ceil(K / 32) in all); with chunks > 1 the product
+// dispatch writes per-chunk FP32 partial sums of C_hi and C_lo
+// ([chunks][M][2][n_pad] floats, workspace_bytes in all) that the merge
+// dispatch reduces in chunk order; with chunks == 1 it writes y itself and
+// needs no workspace.  All fields are 0 when M, N or K is out of range.
+struct GemvPlan {
+    int64_t chunks;
+    int64_t stages;
+    int64_t n_pad;
+    size_t workspace_bytes;
+};
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K);
+
+// Split + both products + merge for 1 <= M <= 8, K >= 0.  `part` (16-byte
+// aligned, part_bytes long) holds the partial sums.  When W does not allow
+// 16-byte buffer loads, or `part` is needed but missing or too small, one
+// fused generic kernel runs instead and `part` is not touched.
+hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
+                       int64_t ldy, int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes,
+                       hipStream_t stream);
 
 }  // namespace cfp32

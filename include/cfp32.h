@@ -22,7 +22,9 @@
  * The guide runs the split and the merge as one dispatch each; these calls
  * map onto that: cfp32_split, cfp32_gemm (two products sharing each W tile,
  * merge fused into its epilogue) and cfp32_merge, plus cfp32_linear, which
- * runs the whole projection (for M <= 8 as one fused kernel).
+ * runs the whole projection (two dispatches at every M: for M <= 8 the
+ * split is done in registers by the product dispatch and the second one
+ * reduces the per-chunk partial sums and merges).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -113,7 +115,10 @@ CFP32_API cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t
                          int64_t M, int64_t N, void *stream);
 
 /* Bytes of device workspace cfp32_linear needs for this shape (0 when none
- * is needed: M <= 8, or an empty problem).  Returns 0 for negative sizes. */
+ * is needed: an empty problem, M, N or K == 0).  Returns 0 for negative
+ * sizes.  M <= 8: about chunks * M * N * 8 bytes of FP32 partial sums, with
+ * at most 256 chunks (1 MiB for M = 1, N = 14336, K = 4096).
+ * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes. */
 CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* The whole projection y = x W (guide: compensated-FP32 paragraph; small
@@ -125,9 +130,14 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         cfp32_linear_workspace_bytes(M, N, K) bytes (may be NULL when that
  *         is 0).  Its contents on entry are ignored; it must not be used by
  *         another call until this call's work on `stream` has completed.
- * M <= 8: one fused kernel (split in registers, both products, merge).
+ * M <= 8: a product kernel (split in registers, both products over row
+ *         chunks of K, FP32 partial sums into the workspace), then a merge
+ *         kernel that sums the chunks in order and merges (two launches).
+ *         W that is not 16-byte aligned with ldw % 8 == 0 takes one fused
+ *         kernel instead, which leaves the workspace untouched.
  * M  > 8: cfp32_split into the workspace, then cfp32_gemm with the merged
  *         epilogue (two launches).
+ * Every path sums in a fixed order: results repeat bit for bit.
  * Results satisfy |y - y_exact| <= 1e-5 * sum_k |x_k w_k| for inputs within
  * the split's domain (|x| < 65520). */
 CFP32_API cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,

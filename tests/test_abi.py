@@ -66,18 +66,32 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     # gemm: no output, or only one of c_hi / c_lo
     assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, None, None, 8, 4, 8, 8, None) == E
     assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, FAKE, None, 8, 4, 8, 8, None) == E
-    # linear: workspace missing or too small for M > 8
-    need = cf.cfp32_linear_workspace_bytes(64, 64, 64)
-    assert need > 0
-    assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, 64, 64, 64, None, 0, None) == E
-    assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, 64, 64, 64, FAKE, need - 1, None) == E
+    # linear: workspace missing or too small, M > 8 and M <= 8
+    for M in (64, 1):
+        need = cf.cfp32_linear_workspace_bytes(M, 64, 64)
+        assert need > 0
+        assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, None, 0, None) == E
+        assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, FAKE, need - 1, None) == E
     # sizes whose extent overflows 64-bit offsets
     big = 1 << 40
     assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
 
 
 def test_workspace_sizes(lib):
-    assert cf.cfp32_linear_workspace_bytes(8, 4096, 4096) == 0        # fused small-M path
+    # M <= 8: FP32 partial sums [chunks][M][2][N rounded up to 512] + 256 B
+    # slack.  512-column tiles, about 256 blocks over tiles x chunks, chunks of
+    # whole 32-row stages; a single chunk merges in place and needs nothing.
+    # M=1, N=14336 (28 tiles), K=4096: 256 // 28 = 9 chunks.
+    assert cf.cfp32_linear_workspace_bytes(1, 14336, 4096) == 9 * 1 * 2 * 14336 * 4 + 256
+    # M=8, N=4096 (8 tiles): 32 chunks of 4 stages.
+    assert cf.cfp32_linear_workspace_bytes(8, 4096, 4096) == 32 * 8 * 2 * 4096 * 4 + 256
+    # M=1, N=5, K=1: one tile, one stage, one chunk.
+    assert cf.cfp32_linear_workspace_bytes(1, 5, 1) == 0
+    # M=4, N=300000 (586 tiles): one chunk.
+    assert cf.cfp32_linear_workspace_bytes(4, 300000, 4096) == 0
+    # M=3, N=1000 (2 tiles), K=777: 128 chunks wanted, ceil(777 / 32) = 25 stages.
+    assert cf.cfp32_linear_workspace_bytes(3, 1000, 777) == 25 * 3 * 2 * 1024 * 4 + 256
+    assert cf.cfp32_linear_workspace_bytes(8, 4096, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(-1, 10, 10) == 0

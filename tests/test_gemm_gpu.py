@@ -224,18 +224,19 @@ def test_gemm_decode_ffn_prefill_full_size():
 
 # -- the whole projection through cfp32_linear ----------------------------------
 
-def run_linear(A, W, x_pad=0, y_pad=0, w_offset=0):
+def run_linear(A, W, x_pad=0, y_pad=0, w_offset=0, w_ld_pad=0):
     M, K = A.shape
     N = W.shape[1]
     xb = np.zeros((M, K + x_pad), np.float32)
     xb[:, :K] = A
-    ldw = N + w_offset
+    ldw = N + w_offset + w_ld_pad
     wb = np.zeros(K * ldw + w_offset, np.uint16)
     wb[w_offset:].reshape(K, ldw)[:, :N] = W.view(np.uint16)
     dx, dw = to_dev(xb), to_dev(wb)
     y = torch.full((M, N + y_pad), 5.0, dtype=torch.float32, device="cuda")
     need = cf.cfp32_linear_workspace_bytes(M, N, K)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    # The workspace's contents on entry must not matter: fill it with NaN bytes.
+    ws = torch.full((max(need, 1),), 0xFF, dtype=torch.uint8, device="cuda")
     st = cf.cfp32_linear(dx.data_ptr(), K + x_pad, dw.data_ptr() + 2 * w_offset, ldw, y.data_ptr(), N + y_pad,
                          M, N, K, ws.data_ptr() if need else None, need, stream_handle())
     assert st == cf.OK, cf.cfp32_status_string(st)
@@ -259,7 +260,7 @@ def test_linear_workloads(name):
 
 
 def test_linear_decode_gemv_full():
-    """M = 1 against the 4096 x 14336 weight: the fused small-M kernel."""
+    """M = 1 against the 4096 x 14336 weight: the small-M path."""
     wl = workloads.decode_ffn_pair(prefill_rows=1)
     A, W = wl.A[0], wl.W
     note("linear decode M=1")
@@ -274,14 +275,29 @@ def test_linear_decode_gemv_full():
 
 @pytest.mark.parametrize("M", range(1, 10))
 def test_linear_small_m_edges(M):
-    """M = 1..8 take the fused kernel, M = 9 the split + GEMM path; ragged N
-    and K, padded leading dimensions and an unaligned weight pointer."""
-    for N, K, w_off in [(777, 1000, 0), (100, 37, 1), (64, 4096, 0), (1, 5, 3)]:
+    """M = 1..8 take the small-M path, M = 9 the split + GEMM path; ragged N
+    and K, padded leading dimensions, and weights that do (ldw % 8 == 0,
+    16-byte aligned: chunked products + merge dispatch) and do not (one
+    generic kernel) allow 16-byte loads."""
+    cases = [  # N, K, pointer offset of W in elements, extra ldw padding
+        (777, 1000, 0, 7),    # aligned, ragged last tile and last chunk
+        (777, 1000, 0, 0),    # ldw % 8 != 0
+        (100, 37, 1, 0),      # unaligned pointer
+        (64, 4096, 0, 0),     # aligned, many chunks
+        (1, 5, 0, 7),         # aligned, one column, fewer rows than waves
+        (1, 5, 3, 0),         # unaligned
+        (2048, 3000, 8, 0),   # aligned pointer offset, several tiles
+        (512, 1, 0, 0),       # one row of W
+        (140000, 100, 0, 0),  # more than 256 column tiles: one chunk, merged in place
+    ]
+    for N, K, w_off, w_ld_pad in cases:
         A, W = workloads.random_case(M * 1000 + N + K, M, K, N, a_scale=100.0)
-        note(f"linear small M={M} N={N} K={K} w_off={w_off}")
-        y = run_linear(A, W, x_pad=3, y_pad=2, w_offset=w_off)
+        note(f"linear small M={M} N={N} K={K} w_off={w_off} w_ld_pad={w_ld_pad}")
+        y = run_linear(A, W, x_pad=3, y_pad=2, w_offset=w_off, w_ld_pad=w_ld_pad)
         y64, abs64 = oracle.y64(A, W)
         assert_within_tolerance(y, y64, abs64, f"M={M} N={N} K={K}")
+        y2 = run_linear(A, W, x_pad=3, y_pad=2, w_offset=w_off, w_ld_pad=w_ld_pad)
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
 
 
 def test_linear_k_zero():
@@ -293,14 +309,15 @@ def test_linear_k_zero():
         assert (to_host(y) == 0).all()
 
 
-def test_linear_rejects_small_workspace_and_enqueues_nothing():
-    A, W = workloads.random_case(1, 64, 64, 64)
+@pytest.mark.parametrize("M", [64, 1])
+def test_linear_rejects_small_workspace_and_enqueues_nothing(M):
+    A, W = workloads.random_case(1, M, 64, 64)
     dx, dw = to_dev(A), to_dev(W)
-    y = torch.full((64, 64), 6.0, dtype=torch.float32, device="cuda")
-    need = cf.cfp32_linear_workspace_bytes(64, 64, 64)
+    y = torch.full((M, 64), 6.0, dtype=torch.float32, device="cuda")
+    need = cf.cfp32_linear_workspace_bytes(M, 64, 64)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    note("linear small workspace")
-    st = cf.cfp32_linear(dx.data_ptr(), 64, dw.data_ptr(), 64, y.data_ptr(), 64, 64, 64, 64,
+    note(f"linear small workspace M={M}")
+    st = cf.cfp32_linear(dx.data_ptr(), 64, dw.data_ptr(), 64, y.data_ptr(), 64, M, 64, 64,
                          ws.data_ptr(), need - 1, stream_handle())
     assert st == cf.ERR_INVALID_VALUE
     assert (to_host(y) == 6.0).all()

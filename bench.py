@@ -4,7 +4,8 @@
 A step is one pass of the whole path over the decode + FFN projection pair
 that shares one FP16 weight W [4096, 14336]:
 
-  1. decode:  y1 = x1 W,  x1 FP32 [1, 4096]      -> cfp32_linear (fused small-M kernel)
+  1. decode:  y1 = x1 W,  x1 FP32 [1, 4096]      -> cfp32_linear (small-M path:
+              K-chunked product dispatch + merge dispatch)
   2. prefill: split(x2) then the dual-product GEMM with the merged epilogue,
               x2 FP32 [8192, 4096]                -> cfp32_split + cfp32_gemm
               (exactly the two launches cfp32_linear makes for M > 8)
@@ -18,9 +19,11 @@ stream inside the timed loop give each kernel's average duration; the MFMA
 roofline is taken for the GEMM, the dominant kernel.
 
 One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
-``headline`` (the 4096^3 GEMM and the M = 1 decode kernel measured on their
-own), ``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded
-sample of the same workload on this host).
+``headline`` (the 4096^3 GEMM and the M = 1 decode path measured on their
+own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
+the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
+``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded sample
+of the same workload on this host).
 """
 from __future__ import annotations
 
@@ -278,6 +281,19 @@ def main():
     check(cf.cfp32_split(xs.data_ptr(), 4096, hs.data_ptr(), ls.data_ptr(), 4096, 4096, 4096, sh), "split")
     sq_us = timed(lambda i: check(cf.cfp32_gemm(hs.data_ptr(), ls.data_ptr(), 4096, ws.data_ptr(), 4096,
                                                 ys.data_ptr(), None, None, 4096, 4096, 4096, 4096, sh), "gemm"), 50)
+    # A/B against true FP32: the whole compensated projection (split + GEMM)
+    # next to the FP32 library GEMM (torch.matmul, FP32 inputs and
+    # accumulation, TF32 off) on the same 4096^3 operands.
+    lin_ws_bytes = cf.cfp32_linear_workspace_bytes(4096, 4096, 4096)
+    lin_ws = torch.empty(lin_ws_bytes, dtype=torch.uint8, device=dev)
+    lin_us = timed(lambda i: check(cf.cfp32_linear(xs.data_ptr(), 4096, ws.data_ptr(), 4096, ys.data_ptr(), 4096,
+                                                   4096, 4096, 4096, lin_ws.data_ptr(), lin_ws_bytes, sh),
+                                   "linear"), 50)
+    torch.backends.cuda.matmul.allow_tf32 = False
+    wf32 = ws.view(torch.float16).float()
+    yf32 = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+    fp32_us = timed(lambda i: torch.matmul(xs, wf32, out=yf32), 20)
+    del lin_ws, wf32, yf32
     torch.cuda.synchronize()
 
     if args.calibration_copy:
@@ -323,6 +339,13 @@ def main():
             "gemv_1x4096x14336_us": round(gemv_us, 2),
             "gemv_GBps": round(dec_bytes / (gemv_us * 1e-6) / 1e9, 1),
             "gemv_frac_hbm": round(dec_bytes / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "fp32_ab_4096": {
+            "cfp32_linear_us": round(lin_us, 2),
+            "cfp32_linear_tflops_fp32eq": round(2 * 4096 ** 3 / (lin_us * 1e-6) / 1e12, 1),
+            "fp32_library_matmul_us": round(fp32_us, 2),
+            "fp32_library_tflops": round(2 * 4096 ** 3 / (fp32_us * 1e-6) / 1e12, 1),
+            "speedup": round(fp32_us / lin_us, 2),
         },
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -170,6 +170,17 @@ cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s));
 
+    // One launch with the split inside the GEMM, where that is faster than the
+    // split kernel plus the GEMM (measured on MI355X: N <= 4096 with at least
+    // 128 output tiles of 128 x 256; for wider N each block's share of the
+    // split, repeated once per 256 columns, outweighs the separate pass, and
+    // small grids are latency-bound).  Both ways multiply the same operands in
+    // the same order, so the results are identical.
+    if (N <= 4096 && ((M + 127) / 128) * ((N + 255) / 256) >= 128) {
+        const hipError_t e = cfp32::launch_gemm_dma_split(x, ldx, w, ldw, y, ldy, M, N, K, s);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
+
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);
     uint16_t *lo = reinterpret_cast<uint16_t *>(base + plane_bytes(M, K));
     const int64_t ldh = split_ld(K);

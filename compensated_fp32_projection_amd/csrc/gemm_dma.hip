@@ -74,6 +74,19 @@ __shared__ uint4 g_stage1[STAGE_SLOTS];
 __shared__ uint4 g_stage2[STAGE_SLOTS];
 __shared__ uint4 g_stage3[STAGE_SLOTS];
 
+// SPLIT variant: the hi and lo planes of A for the stage being multiplied,
+// converted from the FP32 ring once per stage (two buffers, by stage parity;
+// the same layout as the A planes of a ring stage).
+__shared__ uint4 g_conv0[2 * A_SLOTS];
+__shared__ uint4 g_conv1[2 * A_SLOTS];
+
+template <int P>
+__device__ __forceinline__ uint4 *conv_buf()
+{
+    if constexpr (P == 0) return g_conv0;
+    else return g_conv1;
+}
+
 template <int S>
 __device__ __forceinline__ uint4 *stage_buf()
 {
@@ -107,6 +120,7 @@ __device__ __forceinline__ void block_barrier()
 struct DmaArgs {
     const uint16_t *a_hi;
     const uint16_t *a_lo;
+    const float *a32;  // SPLIT variant: FP32 A, split in LDS once per stage
     int64_t lda;
     const uint16_t *w;
     int64_t ldw;
@@ -119,6 +133,22 @@ struct DmaArgs {
     int64_t Ka;  // columns of A that may be read: K, or K rounded up to 8 when A is zero-padded
 };
 
+// FP32 A in LDS (SPLIT variant): each 128-byte row of 32 floats is 8
+// granules, granule g stored at position g ^ (row % 8); eight consecutive
+// lanes reading one granule column then touch eight different 16-byte bank
+// groups.
+__device__ __forceinline__ int a32_slot(int row, int g) { return row * 8 + (g ^ (row & 7)); }
+
+// SPLIT = false: A arrives as the FP16 planes A_hi, A_lo.  SPLIT = true: A
+// arrives as FP32 (same bytes per stage: 128 x 32 x 4 B).  While a wave's
+// MFMAs of stage s run, the wave splits its share of stage s + 1 (the 64 rows
+// its group multiplies, 8 values per lane) with the same split as the
+// standalone split kernel and writes hi and lo to a conversion buffer laid
+// out like the ring's A planes, so both variants multiply identical operands
+// and the split costs each value one conversion per block.  Group g's rows
+// are loaded and converted by group g's own waves only, so the barriers that
+// already separate the two groups' phases order every conversion.
+template <bool SPLIT>
 __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
     const int tid = threadIdx.x;
@@ -135,10 +165,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int64_t m0 = tile_m * BM;
     const int64_t n0 = tile_n * BN;
 
+    // SPLIT: both A resources cover the FP32 matrix (rs_lo is unused).
     const __amdgpu_buffer_rsrc_t rs_hi =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_hi), 0, (int)(g.M * g.lda * 2), kBufferWord3);
+        SPLIT ? __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g.a32), 0, (int)(g.M * g.lda * 4), kBufferWord3)
+              : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_hi), 0, (int)(g.M * g.lda * 2),
+                                                  kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_lo =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_lo), 0, (int)(g.M * g.lda * 2), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(SPLIT ? nullptr : g.a_lo), 0,
+                                          (int)(SPLIT ? 0 : g.M * g.lda * 2), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_w =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
 
@@ -146,14 +180,28 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     // and 64*(2*wave + jj) + lane of W (lane i fills slot base + i).  Byte
     // offsets of stage 0 are formed once; a stage adds 2*k0 (A) or 2*k0*ldw
     // (W).  Granules outside the operands use kNoOffset.
-    int a_off, a_kend, w_off[2], w_kend[2];
-    {
+    // SPLIT: the wave's two A loads are FP32 granules 64*(2*wave + jj) + lane
+    // (8 per row: 4 floats each), a_off[jj] / a_kend[jj].
+    int a_off[2], a_kend[2], w_off[2], w_kend[2];
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int slot = 64 * (2 * wave + jj) + lane;
+            const int row = slot / 8;
+            const int gr = (slot % 8) ^ (row & 7);
+            const bool ok = m0 + row < g.M;
+            a_off[jj] = ok ? (int)(((m0 + row) * g.lda + 4 * gr) * 4) : kNoOffset;
+            a_kend[jj] = ok ? (int)(g.K - 4 * gr) : 0;  // K % 4 == 0: a granule is all in or all out
+        }
+    } else {
         const int slot = 64 * wave + lane;
         const int row = slot / KG;
         const int kg = (slot % KG) ^ ((row >> 2) & 3);
         const bool ok = m0 + row < g.M;
-        a_off = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
-        a_kend = ok ? (int)(g.Ka - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
+        a_off[0] = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
+        a_kend[0] = ok ? (int)(g.Ka - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
+        a_off[1] = a_off[0];
+        a_kend[1] = a_kend[0];
     }
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -169,9 +217,19 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         constexpr int S = decltype(stage_tag)::value;
         uint4 *s = stage_buf<S>();
         const int k0 = (int)k0_64;
-        const int a = k0 < a_kend ? a_off + 2 * k0 : kNoOffset;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0, 0);
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int a = k0 < a_kend[jj] ? a_off[jj] + 4 * k0 : kNoOffset;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * (2 * wave + jj)), 16, a,
+                                                         0, 0, 0);
+            }
+        } else {
+            const int a = k0 < a_kend[0] ? a_off[0] + 2 * k0 : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0,
+                                                     0);
+        }
         const int wstep = (int)(k0_64 * g.ldw * 2);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -195,13 +253,13 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int b_kl = 8 * (lane >> 5) + ((lane & 15) >> 2);                 // + 16 ks + 4 h
     const int b_n0 = wn * WTN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 j
 
-    auto read_frags = [&](const uint4 *s, int ks, Frags &f) {
+    auto read_frags = [&](const uint4 *s, const uint4 *sa, int ks, Frags &f) {
         const int kg = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int row = a_row0 + 32 * i;
-            f.ah[i] = __builtin_bit_cast(half8_t, s[a_slot(0, row, kg)]);
-            f.al[i] = __builtin_bit_cast(half8_t, s[a_slot(1, row, kg)]);
+            f.ah[i] = __builtin_bit_cast(half8_t, sa[a_slot(0, row, kg)]);
+            f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, kg)]);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -227,6 +285,25 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             }
     };
 
+    // SPLIT: lane's conversion unit: row 64*group + u/4, k-granule u%4.
+    auto convert = [&](const uint4 *src, uint4 *dst) {
+        const int u = 64 * (wave & 3) + lane;
+        const int row = 64 * group + (u >> 2);
+        const int kg = u & 3;
+        const floatx4_t v0 = __builtin_bit_cast(floatx4_t, src[a32_slot(row, 2 * kg)]);
+        const floatx4_t v1 = __builtin_bit_cast(floatx4_t, src[a32_slot(row, 2 * kg + 1)]);
+        half8_t h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            _Float16 hh, ll;
+            split_value(e < 4 ? v0[e] : v1[e - 4], hh, ll);
+            h[e] = hh;
+            l[e] = ll;
+        }
+        dst[a_slot(0, row, kg)] = __builtin_bit_cast(uint4, h);
+        dst[a_slot(1, row, kg)] = __builtin_bit_cast(uint4, l);
+    };
+
     const int64_t nk = (g.Ka + BK - 1) / BK;
     Frags f0, f1;
     // One stage for this wave: memory phase, barrier, compute phase, barrier.
@@ -234,13 +311,20 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         constexpr int S = decltype(stage_tag)::value;
         issue(std::integral_constant<int, (S + 3) & 3>{}, (s + 3) * BK);
         const uint4 *buf = stage_buf<S>();
-        read_frags(buf, 0, f0);
-        read_frags(buf, 1, f1);
+        const uint4 *abuf = SPLIT ? conv_buf<S & 1>() : buf;
+        read_frags(buf, abuf, 0, f0);
+        read_frags(buf, abuf, 1, f1);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
         block_barrier();
         __builtin_amdgcn_s_setprio(1);
         mfmas(f0);
         mfmas(f1);
+        if constexpr (SPLIT) {
+            // Stage s + 1 landed (this group's loads) before the barrier above.
+            convert(stage_buf<(S + 1) & 3>(), conv_buf<(S + 1) & 1>());
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));  // the conversion's LDS writes are done
+        }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         block_barrier();
@@ -251,6 +335,12 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     issue(std::integral_constant<int, 2>{}, 2 * BK);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS_PER_WAVE));  // stage 0 landed for this wave
     block_barrier();
+    if constexpr (SPLIT) {
+        convert(stage_buf<0>(), conv_buf<0>());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
+        block_barrier();
+    }
     if (group == 1) block_barrier();  // the second group runs one phase behind
     const int64_t nk4 = nk / NST * NST;
     for (int64_t s0 = 0; s0 < nk4; s0 += NST) {
@@ -309,8 +399,26 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
     if ((M + BM) * lda * 2 >= kLim || (K + BK) * ldw * 2 + (int64_t)BN * 2 >= kLim) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka};
-    gemm_dma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka};
+    gemm_dma_kernel<false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+// The same GEMM reading FP32 A and splitting it while the A fragments are
+// formed (no hi/lo planes in memory, one launch for the whole projection).
+// Needs 16-byte granules of A that lie wholly inside or wholly outside K
+// (K % 4 == 0, lda % 4 == 0, A 16-byte aligned); hipErrorNotSupported
+// otherwise, with nothing enqueued.
+hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w, int64_t ldw, float *y,
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    if (K <= 0 || K % 4 || lda % 4 || ldw % 8 || !aligned16(a) || !aligned16(w)) return hipErrorNotSupported;
+    constexpr int64_t kLim = kNoOffset - (1 << 20);
+    if ((M + BM) * lda * 4 >= kLim || (K + BK) * ldw * 2 + (int64_t)BN * 2 >= kLim) return hipErrorNotSupported;
+    const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
+    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K};
+    gemm_dma_kernel<true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();
 }
 

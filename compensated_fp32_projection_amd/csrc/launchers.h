@@ -28,6 +28,12 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                            int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
 
+// LDS-DMA GEMM on FP32 A, split in registers (one launch for the whole
+// projection); hipErrorNotSupported, with nothing enqueued, unless K % 4 == 0,
+// lda % 4 == 0, ldw % 8 == 0 and A, W are 16-byte aligned.
+hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w, int64_t ldw, float *y,
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 constexpr int64_t kGemvMaxRows = 8;
 
 // Small-M (1 <= M <= 8) path: K is cut into `chunks` row chunks of whole

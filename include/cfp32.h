@@ -22,9 +22,10 @@
  * The guide runs the split and the merge as one dispatch each; these calls
  * map onto that: cfp32_split, cfp32_gemm (two products sharing each W tile,
  * merge fused into its epilogue) and cfp32_merge, plus cfp32_linear, which
- * runs the whole projection (two dispatches at every M: for M <= 8 the
- * split is done in registers by the product dispatch and the second one
- * reduces the per-chunk partial sums and merges).
+ * runs the whole projection in one or two dispatches (for M <= 8 the split
+ * is done in registers by the product dispatch and a second one reduces the
+ * per-chunk partial sums and merges; for M > 8 the split is a dispatch of its
+ * own or, where that is faster, is done by the GEMM as it loads x).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -136,7 +137,11 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         W that is not 16-byte aligned with ldw % 8 == 0 takes one fused
  *         kernel instead, which leaves the workspace untouched.
  * M  > 8: cfp32_split into the workspace, then cfp32_gemm with the merged
- *         epilogue (two launches).
+ *         epilogue (two launches); or, for N <= 4096 with at least 128
+ *         output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0, ldw % 8 == 0,
+ *         x and w 16-byte aligned, one GEMM launch that splits x on the way
+ *         into LDS (the workspace is then not touched).  Both give identical
+ *         bits.
  * Every path sums in a fixed order: results repeat bit for bit.
  * Results satisfy |y - y_exact| <= 1e-5 * sum_k |x_k w_k| for inputs within
  * the split's domain (|x| < 65520). */

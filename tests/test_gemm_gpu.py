@@ -329,3 +329,27 @@ def test_linear_tensor_helper():
     y = cf.linear(to_dev(A), to_dev(W).view(torch.float16))
     y64, abs64 = oracle.y64(A, W)
     assert_within_tolerance(to_host(y), y64, abs64, "helper")
+
+
+@pytest.mark.parametrize("M,K,N", [(8200, 1000, 504), (4096, 4096, 4096), (16384, 256, 296), (8200, 1001, 504),
+                                   (8200, 1000, 500)])
+def test_linear_fused_split_matches_two_launches(M, K, N):
+    """Shapes for which cfp32_linear splits x inside the GEMM (N <= 4096, at
+    least 128 output tiles, K % 4 == 0, ldw % 8 == 0): identical bits to
+    cfp32_split + cfp32_gemm, and within tolerance of the FP64 reference.
+    K = 1001 (partial 16-byte granules of x) and N = ldw = 500 take the
+    two-launch path instead."""
+    A, W = workloads.random_case(M + K + N, M, K, N, a_scale=30.0)
+    note(f"linear fused split {M}x{K}x{N}")
+    y = run_linear(A, W)
+    dx, dw = to_dev(A), to_dev(W)
+    hi = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    lo = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    assert cf.cfp32_split(dx.data_ptr(), K, hi.data_ptr(), lo.data_ptr(), K, M, K, stream_handle()) == cf.OK
+    assert cf.cfp32_gemm(hi.data_ptr(), lo.data_ptr(), K, dw.data_ptr(), N, y2.data_ptr(), None, None, N,
+                         M, N, K, stream_handle()) == cf.OK
+    assert np.array_equal(y.view(np.uint32), to_host(y2).view(np.uint32))
+    rows = np.random.default_rng(M).choice(M, size=min(M, 512), replace=False)
+    y64, abs64 = oracle.y64(A[rows], W)
+    assert_within_tolerance(y[rows], y64, abs64, f"fused {M}x{K}x{N}")

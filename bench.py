@@ -22,6 +22,8 @@ One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
 ``headline`` (the 4096^3 GEMM and the M = 1 decode path measured on their
 own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
 the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
+``separate_add_4096`` (the separate-addition accumulation mode at 4096^3,
+k_per_add 0 = plain accumulation in the same kernel configuration),
 ``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded sample
 of the same workload on this host).
 """
@@ -294,6 +296,13 @@ def main():
     yf32 = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
     fp32_us = timed(lambda i: torch.matmul(xs, wf32, out=yf32), 20)
     del lin_ws, wf32, yf32
+    # The separate-addition accumulation mode at 4096^3 (same split planes),
+    # with plain accumulation in the same kernel configuration as its baseline.
+    sep_us = {}
+    for kpa in (0, 16, 64, 256):
+        sep_us[kpa] = timed(lambda i, kpa=kpa: check(cf.cfp32_gemm_separate_add(
+            hs.data_ptr(), ls.data_ptr(), 4096, ws.data_ptr(), 4096, ys.data_ptr(), None, None, 4096,
+            4096, 4096, 4096, kpa, sh), "separate add"), 10)
     torch.cuda.synchronize()
 
     if args.calibration_copy:
@@ -346,6 +355,10 @@ def main():
             "fp32_library_matmul_us": round(fp32_us, 2),
             "fp32_library_tflops": round(2 * 4096 ** 3 / (fp32_us * 1e-6) / 1e12, 1),
             "speedup": round(fp32_us / lin_us, 2),
+        },
+        "separate_add_4096": {
+            "gemm_us": round(sq_us, 2),
+            **{f"k_per_add_{k}_us": round(v, 2) for k, v in sep_us.items()},
         },
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,

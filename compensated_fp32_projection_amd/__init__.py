@@ -8,8 +8,9 @@ fallback: if the library is missing or the device is not gfx950, calls raise.
 Low-level entry points carry the C names and take raw integers (device
 pointers, sizes, stream handle):
 
-    cfp32_split, cfp32_gemm, cfp32_merge, cfp32_linear,
-    cfp32_linear_workspace_bytes, cfp32_status_string, cfp32_last_hip_error
+    cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
+    cfp32_linear, cfp32_linear_workspace_bytes, cfp32_status_string,
+    cfp32_last_hip_error
 
 Tensor-level helpers (``split``, ``gemm``, ``merge``, ``linear``) check dtype,
 device and layout, pass ``data_ptr()`` and the current stream, and raise
@@ -31,6 +32,7 @@ EXPORTS = (
     "cfp32_last_hip_error",
     "cfp32_split",
     "cfp32_gemm",
+    "cfp32_gemm_separate_add",
     "cfp32_merge",
     "cfp32_linear_workspace_bytes",
     "cfp32_linear",
@@ -67,6 +69,8 @@ def load_library():
     lib.cfp32_split.restype = I32
     lib.cfp32_gemm.argtypes = [P, P, I64, P, I64, P, P, P, I64, I64, I64, I64, P]
     lib.cfp32_gemm.restype = I32
+    lib.cfp32_gemm_separate_add.argtypes = [P, P, I64, P, I64, P, P, P, I64, I64, I64, I64, I64, P]
+    lib.cfp32_gemm_separate_add.restype = I32
     lib.cfp32_merge.argtypes = [P, P, I64, P, I64, I64, I64, P]
     lib.cfp32_merge.restype = I32
     lib.cfp32_linear_workspace_bytes.argtypes = [I64, I64, I64]
@@ -93,6 +97,11 @@ def cfp32_split(x, ldx, hi, lo, ldh, rows, cols, stream) -> int:
 
 def cfp32_gemm(a_hi, a_lo, lda, w, ldw, y, c_hi, c_lo, ldc, M, N, K, stream) -> int:
     return int(load_library().cfp32_gemm(a_hi, a_lo, lda, w, ldw, y, c_hi, c_lo, ldc, M, N, K, stream))
+
+
+def cfp32_gemm_separate_add(a_hi, a_lo, lda, w, ldw, y, c_hi, c_lo, ldc, M, N, K, k_per_add, stream) -> int:
+    return int(load_library().cfp32_gemm_separate_add(a_hi, a_lo, lda, w, ldw, y, c_hi, c_lo, ldc, M, N, K,
+                                                      k_per_add, stream))
 
 
 def cfp32_merge(c_hi, c_lo, ldc, y, ldy, M, N, stream) -> int:

@@ -129,6 +129,26 @@ cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,
                                        /*a_zero_padded=*/false, (hipStream_t)stream));
 }
 
+cfp32_status cfp32_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                                     int64_t ldw, float *y, float *c_hi, float *c_lo, int64_t ldc, int64_t M,
+                                     int64_t N, int64_t K, int64_t k_per_add, void *stream)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
+    if (k_per_add != 0 && k_per_add != 16 && k_per_add != 64 && k_per_add != 256) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if ((c_hi == nullptr) != (c_lo == nullptr)) return CFP32_ERR_INVALID_VALUE;
+    if (!y && !c_hi) return CFP32_ERR_INVALID_VALUE;
+    if (ldc < N || !extent_ok(M, ldc)) return CFP32_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!a_hi || !a_lo || !w || lda < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, lda) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+    }
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_gemm_separate_add(a_hi, a_lo, lda, w, ldw, y, ldc, c_hi, c_lo, ldc, M, N, K,
+                                                    (int)(k_per_add / 16), (hipStream_t)stream));
+}
+
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (!dims_ok(M, N) || !dims_ok(K, 0)) return 0;

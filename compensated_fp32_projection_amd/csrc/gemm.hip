@@ -102,9 +102,18 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 // K stages are fetched with raw buffer loads (no per-load branches; rows past
 // M and columns past N read as zero).  The ragged last stage, and every stage
 // of the generic variant, use guarded loads.
-template <class T, bool AL_A, bool AL_W, bool BUF>
+//
+// SEP > 0 selects the separate-addition accumulation of the laya.cpp Vulkan
+// guide's AMD path (compensated-FP32 paragraph: tile results added with
+// separate FP32 additions, against drift in long multiply-add chains): the
+// matrix unit accumulates SEP consecutive 16-deep k-steps (SEP = 1: each
+// MFMA starts from zero), and each such partial result is added to a running
+// FP32 sum with an ordinary vector addition.  SEP is 1, 4 (one stage) or a
+// multiple of 4.
+template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 {
+    static_assert(SEP == 0 || SEP == 1 || SEP % 4 == 0, "separate additions per MFMA or per whole stages");
     __shared__ uint4 lds[2 * T::LDS_STAGE];
 
     const int tid = threadIdx.x;
@@ -133,13 +142,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 
     floatx16_t acc_hi[T::TM][T::TN];
     floatx16_t acc_lo[T::TM][T::TN];
+    floatx16_t sum_hi[T::TM][T::TN];  // SEP > 0: the running FP32 sums
+    floatx16_t sum_lo[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             acc_hi[i][j] = floatx16_t{};
             acc_lo[i][j] = floatx16_t{};
+            sum_hi[i][j] = floatx16_t{};
+            sum_lo[i][j] = floatx16_t{};
         }
+    // Add the matrix unit's partial sums to the running sums and restart them
+    // from zero (after every k-step for SEP == 1, every SEP k-steps above).
+    auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    sum_hi[i][j][e] += acc_hi[i][j][e];
+                    sum_lo[i][j][e] += acc_lo[i][j][e];
+                }
+                acc_hi[i][j] = floatx16_t{};
+                acc_lo[i][j] = floatx16_t{};
+            }
+    };
 
     uint4 ra[2][T::A_CHUNKS];
     uint4 rw[T::W_ITERS][8];
@@ -254,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     struct Frags {
         half8_t ah[T::TM], al[T::TM], bw[T::TN];
     };
-    auto read_frags = [&](const uint4 *s, int ks, Frags &f) {
+    auto read_frags = [&](const uint4 *s, int ks, Frags &f) __attribute__((always_inline)) {
         const int kg = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
@@ -268,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot<T>(kg, n)]);
         }
     };
-    auto mfmas = [&](const Frags &f) {
+    auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -276,9 +305,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
                 acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
                 acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
             }
+        // SEP == 1: every MFMA started from zero; add its result now.
+        if constexpr (SEP == 1) flush();
     };
     // The fragments of k-step ks+1 are read while the MFMAs of ks run.
-    auto compute_stage = [&](int st) {
+    // Stage kt covers k-steps 4 kt .. 4 kt + 3; with SEP >= 4 the running sums
+    // take the partial sums after every SEP k-steps.
+    auto compute_stage = [&](int st, int64_t kt) __attribute__((always_inline)) {
         const uint4 *s = lds + st * T::LDS_STAGE;
         Frags f[2];
         read_frags(s, 0, f[0]);
@@ -286,6 +319,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         for (int ks = 0; ks < kKG / 2; ++ks) {
             if (ks + 1 < kKG / 2) read_frags(s, ks + 1, f[(ks + 1) & 1]);
             mfmas(f[ks & 1]);
+        }
+        if constexpr (SEP >= 4) {
+            if (((kt + 1) * (kKG / 2)) % SEP == 0) flush();
         }
     };
 
@@ -307,18 +343,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         int64_t kt = 0;
         for (; kt + 1 < nk_full; ++kt) {
             load_stage_buf((kt + 1) * kBK);
-            compute_stage((int)(kt & 1));
+            compute_stage((int)(kt & 1), kt);
             store_stage((int)((kt + 1) & 1));
             __syncthreads();
         }
         for (; kt + 1 < nk; ++kt) {
             load_stage((kt + 1) * kBK);
-            compute_stage((int)(kt & 1));
+            compute_stage((int)(kt & 1), kt);
             store_stage((int)((kt + 1) & 1));
             __syncthreads();
         }
-        compute_stage((int)(kt & 1));
+        compute_stage((int)(kt & 1), kt);
     }
+    if constexpr (SEP >= 4) flush();  // the last, possibly short, group of k-steps
 
     // --- epilogue: 32x32 accumulator layout of v_mfma_f32_32x32x16_f16:
     // lane holds column (lane & 31); element e holds row
@@ -333,7 +370,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = m0 + wm * T::WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (row >= g.M) continue;
-                const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
+                const float h = SEP ? sum_hi[i][j][e] : acc_hi[i][j][e];
+                const float l = SEP ? sum_lo[i][j][e] : acc_lo[i][j][e];
                 if (g.y) g.y[row * g.ldy + col] = merge_value(h, l);
                 if (g.c_hi) {
                     g.c_hi[row * g.ldc + col] = h;
@@ -345,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-template <class T>
+template <class T, int SEP = 0>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
 {
     const int64_t blocks = ((g.M + T::BM - 1) / T::BM) * ((g.N + T::BN - 1) / T::BN);
@@ -358,15 +396,15 @@ hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
     const bool fits = (g.M + T::BM) * g.lda * 2 < kLim && (g.K + kBK) * g.ldw * 2 + (int64_t)T::BN * 2 < kLim;
     const dim3 grid((unsigned)blocks);
     if (al_a && al_w && fits)
-        gemm_kernel<T, true, true, true><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, true, true, SEP><<<grid, kThreads, 0, stream>>>(g);
     else if (al_a && al_w)
-        gemm_kernel<T, true, true, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, true, false, SEP><<<grid, kThreads, 0, stream>>>(g);
     else if (al_a)
-        gemm_kernel<T, true, false, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, false, false, SEP><<<grid, kThreads, 0, stream>>>(g);
     else if (al_w)
-        gemm_kernel<T, false, true, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, true, false, SEP><<<grid, kThreads, 0, stream>>>(g);
     else
-        gemm_kernel<T, false, false, false><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, false, false, SEP><<<grid, kThreads, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -394,6 +432,24 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
     }
     if (tiles_of<TileMedium>(M, N) >= kCus) return launch_tile<TileMedium>(g, stream);
     return launch_tile<TileSmall>(g, stream);
+}
+
+// Separate-addition accumulation (see gemm_kernel): one tile configuration,
+// 64 x 128 (a wave holds 64 running sums next to its 64 accumulators).
+// k_steps_per_add: 0 (plain accumulation in the same configuration, for
+// comparison), 1, 4 or 16 sixteen-deep k-steps per separate addition.
+hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                                    int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
+                                    int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream)
+{
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K};
+    switch (k_steps_per_add) {
+    case 0: return launch_tile<TileMedium, 0>(g, stream);
+    case 1: return launch_tile<TileMedium, 1>(g, stream);
+    case 4: return launch_tile<TileMedium, 4>(g, stream);
+    case 16: return launch_tile<TileMedium, 16>(g, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace cfp32

@@ -22,6 +22,13 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
 
+// Separate-addition accumulation mode: k_steps_per_add is 0 (plain
+// accumulation, same tile configuration), 1, 4 or 16 sixteen-deep k-steps per
+// separate FP32 addition; hipErrorInvalidValue for anything else.
+hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                                    int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
+                                    int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream);
+
 // LDS-DMA variant for aligned operands (gemm_dma.hip); hipErrorNotSupported
 // when the operands do not allow it, in which case nothing was enqueued.
 hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,

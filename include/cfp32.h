@@ -108,6 +108,25 @@ CFP32_API cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, in
                         float *y, float *c_hi, float *c_lo, int64_t ldc,
                         int64_t M, int64_t N, int64_t K, void *stream);
 
+/* Dual-product GEMM with the separate-addition accumulation of the guide's
+ * AMD path (compensated-FP32 paragraph: cooperative-matrix tile results are
+ * added with separate FP32 additions, which reduces the drift of a long dot
+ * product kept entirely inside matrix multiply-adds).  Arguments, outputs and
+ * errors as cfp32_gemm, plus
+ *   k_per_add : 16, 64 or 256 -- the depth of K that the matrix unit
+ *               accumulates on its own before that partial tile result is
+ *               added to a running FP32 sum with an ordinary vector addition
+ *               (16: every MFMA starts from zero); 0 runs the same kernel
+ *               configuration with plain accumulation, for comparison.  Any
+ *               other value gives CFP32_ERR_INVALID_VALUE.
+ * An accuracy mode: one 64 x 128 tile configuration, slower than cfp32_gemm
+ * (the cost is measured next to it).  Fixed order, repeatable bits.  One
+ * kernel launch. */
+CFP32_API cfp32_status cfp32_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,
+                                     const uint16_t *w, int64_t ldw,
+                                     float *y, float *c_hi, float *c_lo, int64_t ldc,
+                                     int64_t M, int64_t N, int64_t K, int64_t k_per_add, void *stream);
+
 /* Standalone merge (guide: split/merge paragraph; one dispatch).
  *   c_hi, c_lo : FP32 [M, N], leading dimension ldc >= N.
  *   y          : FP32 [M, N], leading dimension ldy >= N.

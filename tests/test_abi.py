@@ -63,6 +63,11 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert cf.cfp32_split(FAKE, 3, FAKE, FAKE, 4, 2, 4, None) == E
     assert cf.cfp32_gemm(FAKE, FAKE, 7, FAKE, 8, FAKE, None, None, 8, 4, 8, 8, None) == E
     assert cf.cfp32_merge(FAKE, FAKE, 8, FAKE, 7, 2, 8, None) == E
+    # separate-addition gemm: unsupported depth per addition, missing outputs
+    for kpa in (-16, 8, 32, 128, 512):
+        assert cf.cfp32_gemm_separate_add(FAKE, FAKE, 8, FAKE, 8, FAKE, None, None, 8, 4, 8, 8, kpa, None) == E
+    assert cf.cfp32_gemm_separate_add(FAKE, FAKE, 8, FAKE, 8, None, None, None, 8, 4, 8, 8, 16, None) == E
+    assert cf.cfp32_gemm_separate_add(FAKE, FAKE, 7, FAKE, 8, FAKE, None, None, 8, 4, 8, 8, 16, None) == E
     # gemm: no output, or only one of c_hi / c_lo
     assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, None, None, 8, 4, 8, 8, None) == E
     assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, None, FAKE, None, 8, 4, 8, 8, None) == E
@@ -103,6 +108,7 @@ def test_workspace_sizes(lib):
 def test_empty_problems_are_no_ops(lib):
     assert cf.cfp32_split(None, 0, None, None, 0, 0, 5, None) == cf.OK
     assert cf.cfp32_gemm(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, None) == cf.OK
+    assert cf.cfp32_gemm_separate_add(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, 64, None) == cf.OK
     assert cf.cfp32_merge(None, None, 0, None, 0, 4, 0, None) == cf.OK
     assert cf.cfp32_linear(None, 0, None, 0, None, 0, 0, 8, 8, None, 0, None) == cf.OK
 

@@ -9,8 +9,8 @@ Low-level entry points carry the C names and take raw integers (device
 pointers, sizes, stream handle):
 
     cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
-    cfp32_linear, cfp32_linear_workspace_bytes, cfp32_status_string,
-    cfp32_last_hip_error
+    cfp32_linear, cfp32_linear_workspace_bytes, cfp32_linear_ex,
+    cfp32_linear_ex_workspace_bytes, cfp32_status_string, cfp32_last_hip_error
 
 Tensor-level helpers (``split``, ``gemm``, ``merge``, ``linear``) check dtype,
 device and layout, pass ``data_ptr()`` and the current stream, and raise
@@ -36,7 +36,11 @@ EXPORTS = (
     "cfp32_merge",
     "cfp32_linear_workspace_bytes",
     "cfp32_linear",
+    "cfp32_linear_ex_workspace_bytes",
+    "cfp32_linear_ex",
 )
+
+W_KN, W_NK = 0, 1
 
 
 class Cfp32Error(RuntimeError):
@@ -77,6 +81,10 @@ def load_library():
     lib.cfp32_linear_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.cfp32_linear.restype = I32
+    lib.cfp32_linear_ex_workspace_bytes.argtypes = [I64, I64, I64, I32]
+    lib.cfp32_linear_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.cfp32_linear_ex.argtypes = [P, I64, P, I64, I32, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.cfp32_linear_ex.restype = I32
     _lib = lib
     return lib
 
@@ -114,6 +122,15 @@ def cfp32_linear_workspace_bytes(M, N, K) -> int:
 
 def cfp32_linear(x, ldx, w, ldw, y, ldy, M, N, K, workspace, workspace_bytes, stream) -> int:
     return int(load_library().cfp32_linear(x, ldx, w, ldw, y, ldy, M, N, K, workspace, workspace_bytes, stream))
+
+
+def cfp32_linear_ex_workspace_bytes(M, N, K, w_layout) -> int:
+    return int(load_library().cfp32_linear_ex_workspace_bytes(M, N, K, w_layout))
+
+
+def cfp32_linear_ex(x, ldx, w, ldw, w_layout, bias, y, ldy, M, N, K, workspace, workspace_bytes, stream) -> int:
+    return int(load_library().cfp32_linear_ex(x, ldx, w, ldw, w_layout, bias, y, ldy, M, N, K, workspace,
+                                              workspace_bytes, stream))
 
 
 # -- tensor helpers -------------------------------------------------------------
@@ -233,20 +250,33 @@ class Workspace:
 _default_ws = Workspace()
 
 
-def linear(x, w, out=None, workspace: Workspace | None = None, stream=None):
-    """y = x W with the compensated-FP32 method: x FP32 [M,K], w FP16 [K,N]."""
+def linear(x, w, out=None, workspace: Workspace | None = None, stream=None, bias=None, w_layout: str = "kn"):
+    """y = x W (+ bias) with the compensated-FP32 method: x FP32 [M,K]; w FP16
+    [K,N] (w_layout "kn") or [N,K] ("nk", a torch.nn.Linear weight); bias
+    FP32 [N] or None."""
     torch = _torch()
+    if w_layout not in ("kn", "nk"):
+        raise ValueError("w_layout must be 'kn' or 'nk'")
     px, M, K, ldx = _mat(x, (torch.float32,), "x")
-    pw, K2, N, ldw = _mat(w, _f16_dtypes(), "w")
+    pw, r, c, ldw = _mat(w, _f16_dtypes(), "w")
+    K2, N = (r, c) if w_layout == "kn" else (c, r)
     if K2 != K:
         raise ValueError("inner dimensions differ")
+    pb = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.device != x.device or bias.dim() != 1 or bias.shape[0] != N \
+                or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous FP32 [N] tensor on x's device")
+        pb = bias.data_ptr()
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
     py, M3, N3, ldy = _mat(out, (torch.float32,), "out")
     if (M3, N3) != (M, N):
         raise ValueError("out has the wrong shape")
-    need = cfp32_linear_workspace_bytes(M, N, K)
+    layout = W_KN if w_layout == "kn" else W_NK
+    need = cfp32_linear_ex_workspace_bytes(M, N, K, layout)
     ws = (workspace or _default_ws).get(need, x.device)
     pws = ws.data_ptr() if ws is not None else None
-    _check(cfp32_linear(px, ldx, pw, ldw, py, ldy, M, N, K, pws, need, _stream(stream)), "cfp32_linear")
+    _check(cfp32_linear_ex(px, ldx, pw, ldw, layout, pb, py, ldy, M, N, K, pws, need, _stream(stream)),
+           "cfp32_linear_ex")
     return out

@@ -149,12 +149,14 @@ cfp32_status cfp32_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo,
                                                     (int)(k_per_add / 16), (hipStream_t)stream));
 }
 
-size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
+size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K, int w_layout)
 {
+    if (w_layout != CFP32_W_KN && w_layout != CFP32_W_NK) return 0;
     if (!dims_ok(M, N) || !dims_ok(K, 0)) return 0;
     if (M == 0 || N == 0 || K == 0) return 0;
     // + kAlign: slack to realign the caller's pointer.
     if (M <= cfp32::kGemvMaxRows) {
+        if (w_layout == CFP32_W_NK) return 0;  // one dispatch, no partial sums
         const size_t b = cfp32::gemv_plan(M, N, K).workspace_bytes;
         return b == 0 ? 0 : b + kAlign;
     }
@@ -162,33 +164,43 @@ size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return 2 * plane_bytes(M, K) + kAlign;
 }
 
-cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
-                          int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
-                          size_t workspace_bytes, void *stream)
+size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
+    return cfp32_linear_ex_workspace_bytes(M, N, K, CFP32_W_KN);
+}
+
+cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int w_layout,
+                             const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (w_layout != CFP32_W_KN && w_layout != CFP32_W_NK) return CFP32_ERR_INVALID_VALUE;
+    const bool nk = w_layout == CFP32_W_NK;
     if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
     if (M == 0 || N == 0) return CFP32_OK;
     if (!y || ldy < N || !extent_ok(M, ldy)) return CFP32_ERR_INVALID_VALUE;
     if (K > 0) {
-        if (!x || !w || ldx < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
-        if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+        if (!x || !w || ldx < K || ldw < (nk ? K : N)) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, ldx) || !extent_ok(nk ? N : K, ldw)) return CFP32_ERR_INVALID_VALUE;
     }
-    const size_t need = cfp32_linear_workspace_bytes(M, N, K);
+    const size_t need = cfp32_linear_ex_workspace_bytes(M, N, K, w_layout);
     if (need > 0 && (!workspace || workspace_bytes < need)) return CFP32_ERR_INVALID_VALUE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
     hipStream_t s = (hipStream_t)stream;
 
     const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
+    if (M <= cfp32::kGemvMaxRows && nk)
+        return launched(cfp32::launch_gemv_nk(x, ldx, w, ldw, y, ldy, M, N, K, s, bias));
     if (M <= cfp32::kGemvMaxRows) {
         // need == 0: K == 0, or K is one chunk and the product kernel merges itself.
         float *part = need > 0 ? reinterpret_cast<float *>(base) : nullptr;
-        return launched(cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, part, need > 0 ? need - kAlign : 0, s));
+        return launched(cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, part, need > 0 ? need - kAlign : 0, s,
+                                           bias));
     }
 
     if (K == 0)  // nothing to split: the product of an empty sum is +0
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
-                                           N, 0, false, s));
+                                           N, 0, false, s, bias));
 
     // One launch with the split inside the GEMM, where that is faster than the
     // split kernel plus the GEMM (measured on MI355X: N <= 4096 with at least
@@ -197,7 +209,7 @@ cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_
     // small grids are latency-bound).  Both ways multiply the same operands in
     // the same order, so the results are identical.
     if (N <= 4096 && ((M + 127) / 128) * ((N + 255) / 256) >= 128) {
-        const hipError_t e = cfp32::launch_gemm_dma_split(x, ldx, w, ldw, y, ldy, M, N, K, s);
+        const hipError_t e = cfp32::launch_gemm_dma_split(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
         if (e != hipErrorNotSupported) return launched(e);
     }
 
@@ -209,7 +221,15 @@ cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_
     hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, ldh, s);
     if (e != hipSuccess) return hip_fail(e);
     return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K,
-                                       /*a_zero_padded=*/true, s));
+                                       /*a_zero_padded=*/true, s, bias, nk));
+}
+
+cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
+                          int64_t ldy, int64_t M, int64_t N, int64_t K, void *workspace,
+                          size_t workspace_bytes, void *stream)
+{
+    return cfp32_linear_ex(x, ldx, w, ldw, CFP32_W_KN, nullptr, y, ldy, M, N, K, workspace, workspace_bytes,
+                           stream);
 }
 
 }  // extern "C"

@@ -58,6 +58,8 @@ struct TileCfg {
     static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile is whole MFMA blocks");
     static_assert((BM * kKG) % kThreads == 0, "A stage splits evenly over the threads");
     static_assert(W_BLOCKS % 64 == 0, "W loaders are whole waves");
+    static constexpr int W_NK_CHUNKS = kKG * BN / kThreads;  // [N, K] W: 16-byte loads per thread per stage
+    static_assert(W_NK_CHUNKS <= 8 * W_ITERS && (kKG * BN) % kThreads == 0, "[N, K] granules fit the W registers");
     static_assert(2 * LDS_STAGE * 16 <= 160 * 1024, "double-buffered stage fits in LDS");
 };
 
@@ -77,6 +79,7 @@ struct GemmArgs {
     float *c_lo;
     int64_t ldc;
     int64_t M, N, K;
+    const float *bias;  // FP32 [N] added to y after the merge, or null
 };
 
 // Slot of A granule (k-group kg, tile row `row`) of plane p inside a stage.
@@ -110,7 +113,10 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 // MFMA starts from zero), and each such partial result is added to a running
 // FP32 sum with an ordinary vector addition.  SEP is 1, 4 (one stage) or a
 // multiple of 4.
-template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0>
+//
+// WNK: W is given as [N, K] (ldw >= K); its 16-byte k-granules are loaded and
+// stored exactly like those of A, no transpose needed.
+template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0, bool WNK = false>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 {
     static_assert(SEP == 0 || SEP == 1 || SEP % 4 == 0, "separate additions per MFMA or per whole stages");
@@ -181,9 +187,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     const __amdgpu_buffer_rsrc_t rs_lo =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_lo), 0, (int)(g.M * g.lda * 2), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_w =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)((WNK ? g.N : g.K) * g.ldw * 2),
+                                          kBufferWord3);
     int voff_a[T::A_CHUNKS];
     int voff_w[T::W_ITERS];
+    int voff_wn[T::W_NK_CHUNKS];  // WNK: like voff_a, granule q of column (c >> 3)
+    if constexpr (BUF && WNK) {
+#pragma unroll
+        for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+            const int c = tid + kThreads * q;
+            const int64_t gn = n0 + (c >> 3);
+            voff_wn[q] = gn < g.N ? (int)((gn * g.ldw + 8 * (c & 7)) * 2) : kNoOffset;
+        }
+    }
     if constexpr (BUF) {
 #pragma unroll
         for (int i = 0; i < T::A_CHUNKS; ++i) {
@@ -205,6 +221,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         for (int i = 0; i < T::A_CHUNKS; ++i) {
             ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], (int)(k0 * 2), 0));
             ra[1][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, voff_a[i], (int)(k0 * 2), 0));
+        }
+        if constexpr (WNK) {
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q)
+                rw[q >> 3][q & 7] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_wn[q], (int)(k0 * 2), 0));
+            return;
         }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
@@ -231,6 +254,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
                 ra[1][i] = make_uint4(0, 0, 0, 0);
             }
         }
+        if constexpr (WNK) {
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+                const int c = tid + kThreads * q;
+                const int64_t gn = n0 + (c >> 3), gk = k0 + 8 * (c & 7);
+                rw[q >> 3][q & 7] = gn < g.N ? load_row8<AL_W>(g.w + gn * g.ldw, gk, g.K) : make_uint4(0, 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
             const int b = tid + kThreads * j;
@@ -254,6 +286,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             const int kg = c & 7, row = c >> 3;
             s[a_slot<T>(0, kg, row)] = ra[0][i];
             s[a_slot<T>(1, kg, row)] = ra[1][i];
+        }
+        if constexpr (WNK) {
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+                const int c = tid + kThreads * q;
+                s[w_slot<T>(c & 7, c >> 3)] = rw[q >> 3][q & 7];
+            }
+            return;
         }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
@@ -372,7 +412,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
                 if (row >= g.M) continue;
                 const float h = SEP ? sum_hi[i][j][e] : acc_hi[i][j][e];
                 const float l = SEP ? sum_lo[i][j][e] : acc_lo[i][j][e];
-                if (g.y) g.y[row * g.ldy + col] = merge_value(h, l);
+                if (g.y) {
+                    float v = merge_value(h, l);
+                    if (g.bias) v = v + g.bias[col];
+                    g.y[row * g.ldy + col] = v;
+                }
                 if (g.c_hi) {
                     g.c_hi[row * g.ldc + col] = h;
                     g.c_lo[row * g.ldc + col] = l;
@@ -383,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-template <class T, int SEP = 0>
+template <class T, int SEP = 0, bool WNK = false>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
 {
     const int64_t blocks = ((g.M + T::BM - 1) / T::BM) * ((g.N + T::BN - 1) / T::BN);
@@ -393,18 +437,20 @@ hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
     // Buffer offsets are 32-bit: every byte offset a thread forms, including a
     // tile's overhang past M and N, must stay below kNoOffset.
     constexpr int64_t kLim = kNoOffset - (1 << 20);
-    const bool fits = (g.M + T::BM) * g.lda * 2 < kLim && (g.K + kBK) * g.ldw * 2 + (int64_t)T::BN * 2 < kLim;
+    const bool fits = (g.M + T::BM) * g.lda * 2 < kLim &&
+                      (WNK ? (g.N + T::BN) * g.ldw * 2 + (int64_t)kBK * 2 < kLim
+                           : (g.K + kBK) * g.ldw * 2 + (int64_t)T::BN * 2 < kLim);
     const dim3 grid((unsigned)blocks);
     if (al_a && al_w && fits)
-        gemm_kernel<T, true, true, true, SEP><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, true, true, SEP, WNK><<<grid, kThreads, 0, stream>>>(g);
     else if (al_a && al_w)
-        gemm_kernel<T, true, true, false, SEP><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, true, false, SEP, WNK><<<grid, kThreads, 0, stream>>>(g);
     else if (al_a)
-        gemm_kernel<T, true, false, false, SEP><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, true, false, false, SEP, WNK><<<grid, kThreads, 0, stream>>>(g);
     else if (al_w)
-        gemm_kernel<T, false, true, false, SEP><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, true, false, SEP, WNK><<<grid, kThreads, 0, stream>>>(g);
     else
-        gemm_kernel<T, false, false, false, SEP><<<grid, kThreads, 0, stream>>>(g);
+        gemm_kernel<T, false, false, false, SEP, WNK><<<grid, kThreads, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -420,18 +466,20 @@ int64_t tiles_of(int64_t M, int64_t N)
 // (256 CUs); below that, the smallest tile, which has the most blocks.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream)
+                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
+                       const float *bias, bool w_nk)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias};
     constexpr int64_t kCus = 256;
     if (tiles_of<TileLarge>(M, N) >= kCus) {
         const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
-                                             a_zero_padded, stream);
+                                             a_zero_padded, stream, bias, w_nk);
         if (e != hipErrorNotSupported) return e;
-        return launch_tile<TileLarge>(g, stream);
+        return w_nk ? launch_tile<TileLarge, 0, true>(g, stream) : launch_tile<TileLarge>(g, stream);
     }
-    if (tiles_of<TileMedium>(M, N) >= kCus) return launch_tile<TileMedium>(g, stream);
-    return launch_tile<TileSmall>(g, stream);
+    if (tiles_of<TileMedium>(M, N) >= kCus)
+        return w_nk ? launch_tile<TileMedium, 0, true>(g, stream) : launch_tile<TileMedium>(g, stream);
+    return w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
 }
 
 // Separate-addition accumulation (see gemm_kernel): one tile configuration,
@@ -442,7 +490,7 @@ hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, 
                                     int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                                     int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr};
     switch (k_steps_per_add) {
     case 0: return launch_tile<TileMedium, 0>(g, stream);
     case 1: return launch_tile<TileMedium, 1>(g, stream);

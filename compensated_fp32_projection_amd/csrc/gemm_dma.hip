@@ -106,6 +106,11 @@ __device__ __forceinline__ int w_slot(int k, int ng)
     return 2 * A_SLOTS + k * WG + (ng ^ ((k & 3) << 2));
 }
 
+// WNK variant (W given as [N, K], K-contiguous): W sits in LDS like A, as
+// 16-byte k-granules of each of the 256 columns, the granule order XOR-ed with
+// bits of the column index; an MFMA B fragment is one ds_read_b128.
+__device__ __forceinline__ int w_slot_nk(int n, int kg) { return 2 * A_SLOTS + n * KG + (kg ^ ((n >> 2) & 3)); }
+
 // s_waitcnt immediates (gfx9 encoding): vector-memory count N, LDS count 0 or any.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -131,6 +136,7 @@ struct DmaArgs {
     int64_t ldc;
     int64_t M, N, K;
     int64_t Ka;  // columns of A that may be read: K, or K rounded up to 8 when A is zero-padded
+    const float *bias;  // FP32 [N] added to y after the merge, or null
 };
 
 // FP32 A in LDS (SPLIT variant): each 128-byte row of 32 floats is 8
@@ -148,7 +154,8 @@ __device__ __forceinline__ int a32_slot(int row, int g) { return row * 8 + (g ^ 
 // and the split costs each value one conversion per block.  Group g's rows
 // are loaded and converted by group g's own waves only, so the barriers that
 // already separate the two groups' phases order every conversion.
-template <bool SPLIT>
+// WNK = true: W is [N, K] (ldw >= K, K % 8 == 0), else [K, N].
+template <bool SPLIT, bool WNK>
 __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
     const int tid = threadIdx.x;
@@ -174,7 +181,8 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(SPLIT ? nullptr : g.a_lo), 0,
                                           (int)(SPLIT ? 0 : g.M * g.lda * 2), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_w =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)((WNK ? g.N : g.K) * g.ldw * 2),
+                                          kBufferWord3);
 
     // This wave's loads of a stage: granules 64*wave + lane of each A plane
     // and 64*(2*wave + jj) + lane of W (lane i fills slot base + i).  Byte
@@ -206,11 +214,19 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
         const int slot = 64 * (2 * wave + jj) + lane;
-        const int k = slot / WG;
-        const int ng = (slot % WG) ^ ((k & 3) << 2);
-        const bool ok = n0 + 8 * ng < g.N;
-        w_off[jj] = ok ? (int)((k * g.ldw + n0 + 8 * ng) * 2) : kNoOffset;
-        w_kend[jj] = ok ? (int)(g.K - k) : 0;
+        if constexpr (WNK) {
+            const int n = slot / KG;
+            const int kg = (slot % KG) ^ ((n >> 2) & 3);
+            const bool ok = n0 + n < g.N;
+            w_off[jj] = ok ? (int)(((n0 + n) * g.ldw + 8 * kg) * 2) : kNoOffset;
+            w_kend[jj] = ok ? (int)(g.K - 8 * kg) : 0;  // K % 8 == 0: a granule is all in or all out
+        } else {
+            const int k = slot / WG;
+            const int ng = (slot % WG) ^ ((k & 3) << 2);
+            const bool ok = n0 + 8 * ng < g.N;
+            w_off[jj] = ok ? (int)((k * g.ldw + n0 + 8 * ng) * 2) : kNoOffset;
+            w_kend[jj] = ok ? (int)(g.K - k) : 0;
+        }
     }
 
     auto issue = [&](auto stage_tag, int64_t k0_64) {
@@ -230,7 +246,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0,
                                                      0);
         }
-        const int wstep = (int)(k0_64 * g.ldw * 2);
+        const int wstep = WNK ? 2 * k0 : (int)(k0_64 * g.ldw * 2);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int o = k0 < w_kend[jj] ? w_off[jj] + wstep : kNoOffset;
@@ -252,6 +268,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int a_row0 = wm * WTM + (lane & 31);
     const int b_kl = 8 * (lane >> 5) + ((lane & 15) >> 2);                 // + 16 ks + 4 h
     const int b_n0 = wn * WTN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 j
+    const int b_col0 = wn * WTN + (lane & 31);                             // WNK: + 32 j
 
     auto read_frags = [&](const uint4 *s, const uint4 *sa, int ks, Frags &f) {
         const int kg = 2 * ks + (lane >> 5);
@@ -260,6 +277,12 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             const int row = a_row0 + 32 * i;
             f.ah[i] = __builtin_bit_cast(half8_t, sa[a_slot(0, row, kg)]);
             f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, kg)]);
+        }
+        if constexpr (WNK) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot_nk(b_col0 + 32 * j, kg)]);
+            return;
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -370,7 +393,11 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
                 const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
                 // Outputs are written once: non-temporal stores keep them from
                 // evicting the A and W panels other tiles still read from L2.
-                if (g.y) __builtin_nontemporal_store(merge_value(h, l), g.y + row * g.ldy + col);
+                if (g.y) {
+                    float v = merge_value(h, l);
+                    if (g.bias) v = v + g.bias[col];
+                    __builtin_nontemporal_store(v, g.y + row * g.ldy + col);
+                }
                 if (g.c_hi) {
                     __builtin_nontemporal_store(h, g.c_hi + row * g.ldc + col);
                     __builtin_nontemporal_store(l, g.c_lo + row * g.ldc + col);
@@ -381,6 +408,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// Every byte offset a lane forms into W (including a tile's overhang past K
+// or N) stays below kNoOffset.
+inline bool w_fits(int64_t ldw, int64_t N, int64_t K, bool w_nk)
+{
+    constexpr int64_t kLim = kNoOffset - (1 << 20);
+    return w_nk ? (N + BN) * ldw * 2 + (int64_t)BK * 2 < kLim : (K + BK) * ldw * 2 + (int64_t)BN * 2 < kLim;
+}
+
 }  // namespace
 
 // Runs the LDS-DMA kernel when the operands allow it; returns
@@ -388,19 +423,24 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 // columns of A from K up to the next multiple of 8 hold +0 and may be read.
 hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                           int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream)
+                           int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
+                           const float *bias, bool w_nk)
 {
     if (K <= 0 || lda % 8 || ldw % 8 || !aligned16(a_hi) || !aligned16(a_lo) || !aligned16(w))
         return hipErrorNotSupported;
+    if (w_nk && K % 8) return hipErrorNotSupported;
     const int64_t Ka = (K % 8 == 0) ? K : (a_zero_padded ? (K + 7) / 8 * 8 : -1);
     if (Ka < 0 || Ka > lda) return hipErrorNotSupported;
     // Every byte offset a lane forms (including a tile's overhang) stays below kNoOffset.
     constexpr int64_t kLim = kNoOffset - (1 << 20);
-    if ((M + BM) * lda * 2 >= kLim || (K + BK) * ldw * 2 + (int64_t)BN * 2 >= kLim) return hipErrorNotSupported;
+    if ((M + BM) * lda * 2 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka};
-    gemm_dma_kernel<false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias};
+    if (w_nk)
+        gemm_dma_kernel<false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    else
+        gemm_dma_kernel<false, false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -410,15 +450,20 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
 // (K % 4 == 0, lda % 4 == 0, A 16-byte aligned); hipErrorNotSupported
 // otherwise, with nothing enqueued.
 hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w, int64_t ldw, float *y,
-                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream)
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                                 const float *bias, bool w_nk)
 {
     if (K <= 0 || K % 4 || lda % 4 || ldw % 8 || !aligned16(a) || !aligned16(w)) return hipErrorNotSupported;
+    if (w_nk && K % 8) return hipErrorNotSupported;
     constexpr int64_t kLim = kNoOffset - (1 << 20);
-    if ((M + BM) * lda * 4 >= kLim || (K + BK) * ldw * 2 + (int64_t)BN * 2 >= kLim) return hipErrorNotSupported;
+    if ((M + BM) * lda * 4 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K};
-    gemm_dma_kernel<true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K, bias};
+    if (w_nk)
+        gemm_dma_kernel<true, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    else
+        gemm_dma_kernel<true, false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();
 }
 

@@ -117,6 +117,7 @@ struct GemvArgs {
     int64_t stages;   // ceil(K / 32)
     int64_t chunks;   // the stages split as evenly as possible, in order
     int64_t ntiles;   // ceil(N / 512)
+    const float *bias;  // FP32 [N] added to y after the merge, or null
 };
 
 __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
@@ -262,7 +263,11 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
             const int64_t n = col0 + 16 * t;
             const float ch = acc[t][2 * q], cl = acc[t][2 * q + 1];
             if (g.chunks == 1) {
-                if (n < g.N) __builtin_nontemporal_store(merge_value(ch, cl), g.y + m * g.ldy + n);
+                if (n < g.N) {
+                    float v = merge_value(ch, cl);
+                    if (g.bias) v = v + g.bias[n];
+                    __builtin_nontemporal_store(v, g.y + m * g.ldy + n);
+                }
             } else {
                 // Streaming stores: the merge dispatch reads these from
                 // memory anyway (they come from every XCD).
@@ -282,7 +287,8 @@ constexpr int kMergeBatch = 16;
 
 __global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict__ part, int64_t n_pad,
                                                          int64_t chunks, int M, int64_t N,
-                                                         float *__restrict__ y, int64_t ldy)
+                                                         float *__restrict__ y, int64_t ldy,
+                                                         const float *__restrict__ bias)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)M * N) return;
@@ -307,7 +313,9 @@ __global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict
             }
         }
     }
-    __builtin_nontemporal_store(merge_value(th, tl), y + m * ldy + n);
+    float v = merge_value(th, tl);
+    if (bias) v = v + bias[n];
+    __builtin_nontemporal_store(v, y + m * ldy + n);
 }
 
 // Fallback for W that is not 16-byte aligned or too large for 32-bit buffer
@@ -320,7 +328,8 @@ template <int MR>
 __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const float *__restrict__ x, int64_t ldx,
                                                                        const uint16_t *__restrict__ w, int64_t ldw,
                                                                        float *__restrict__ y, int64_t ldy,
-                                                                       int64_t N, int64_t K)
+                                                                       int64_t N, int64_t K,
+                                                                       const float *__restrict__ bias)
 {
     constexpr int CH = kGenericNB / 8;
     constexpr int KL = kGenericThreads / CH;
@@ -388,8 +397,143 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
             th += red[v][col >> 3][m][col & 7][0];
             tl += red[v][col >> 3][m][col & 7][1];
         }
-        y[m * ldy + gn] = merge_value(th, tl);
+        float v = merge_value(th, tl);
+        if (bias) v = v + bias[gn];
+        y[m * ldy + gn] = v;
     }
+}
+
+// ---- W given as [N, K] (a torch.nn.Linear weight: each output column's
+// weights are one K-contiguous row) ----------------------------------------
+//
+// Every output column streams its own row of W, so no column strip problem
+// arises and no partial sums cross blocks: one dispatch.  A wave owns 16
+// columns over all of K; per 32-deep k-step, lane l loads 16 bytes of row
+// nb + l % 16 at k = 8 (l / 16) (exactly its MFMA B fragment, no LDS) and the
+// 8 matching values of x (two 16-byte loads), splits them and feeds one
+// v_mfma_f32_16x16x32_f16 with the hi and lo rows interleaved as above.
+// kNkU k-steps of loads are in flight per wave.  The K-reduction of each
+// output stays inside one MFMA chain, and the merge (and bias) happen in the
+// lane that holds both rows.  Needs K % 8 == 0 (a 16-byte granule is all in
+// or all out), W and x 16-byte aligned with ldw % 8 == 0 and ldx % 4 == 0.
+constexpr int kNkU = 8;
+
+__global__ __launch_bounds__(256) void gemv_nk_kernel(const float *__restrict__ x, int64_t ldx,
+                                                      const uint16_t *__restrict__ w, int64_t ldw,
+                                                      float *__restrict__ y, int64_t ldy,
+                                                      const float *__restrict__ bias, int M, int64_t N, int64_t K)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * 16;
+    if (nb >= N) return;  // wave-uniform
+    const int64_t n = nb + (lane & 15);
+    const int kq = lane >> 4;
+    const int ai = lane & 15;
+    const int am = ai >> 1;
+    const bool a_lo = ai & 1;
+
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0, (int)(N * ldw * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs_x =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), 0, (int)(M * ldx * 4), kBufferWord3);
+    // Granule k = k0 + 8 kq of this lane's W row and x row, while k < K.
+    const int w_base = n < N ? (int)((n * ldw + 8 * kq) * 2) : 0;
+    const int x_base = am < M ? (int)((am * ldx + 8 * kq) * 4) : 0;
+    const int w_kend = n < N ? (int)K - 8 * kq : INT_MIN;
+    const int x_kend = am < M ? (int)K - 8 * kq : INT_MIN;
+
+    floatx4_t acc = floatx4_t{};
+    for (int k0 = 0; k0 < (int)K; k0 += 32 * kNkU) {
+        uint4 wv[kNkU];
+        floatx4_t xa[kNkU], xb[kNkU];
+#pragma unroll
+        for (int u = 0; u < kNkU; ++u) {
+            const int k = k0 + 32 * u;
+            const int ox = k < x_kend ? x_base + 4 * k : kNoOffset;
+            xa[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 0, 0));
+            xb[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 16, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kNkU; ++u) {
+            const int k = k0 + 32 * u;
+            const int ow = k < w_kend ? w_base + 2 * k : kNoOffset;
+            wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, ow, 0, kStreamAux));
+        }
+#pragma unroll
+        for (int u = 0; u < kNkU; ++u) {
+            half8_t a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                _Float16 h, l;
+                split_value(e < 4 ? xa[u][e] : xb[u][e - 4], h, l);  // rows past M read 0: (0, 0)
+                a[e] = a_lo ? l : h;
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, wv[u]), acc, 0, 0, 0);
+        }
+    }
+    // 16x16 accumulator: rows 4 kq + e, column lane % 16; rows 2m, 2m + 1 are
+    // hi, lo of x row m.
+    if (n >= N) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int m = 2 * kq + q;
+        if (m >= M) continue;
+        float v = merge_value(acc[2 * q], acc[2 * q + 1]);
+        if (bias) v = v + bias[n];
+        y[m * ldy + n] = v;
+    }
+}
+
+// [N, K] fallback for any alignment and K: a wave per output column, lanes
+// striding K, FP32 FMAs, a fixed-order butterfly over the wave.
+template <int MR>
+__global__ __launch_bounds__(256) void gemv_nk_generic_kernel(const float *__restrict__ x, int64_t ldx,
+                                                              const uint16_t *__restrict__ w, int64_t ldw,
+                                                              float *__restrict__ y, int64_t ldy,
+                                                              const float *__restrict__ bias, int64_t N, int64_t K)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N) return;  // wave-uniform
+    float sh[MR], sl[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) sh[m] = 0.0f, sl[m] = 0.0f;
+    for (int64_t k = lane; k < K; k += 64) {
+        const float wf = half_bits_to_float(w[n * ldw + k]);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            _Float16 h16, l16;
+            split_value(x[m * ldx + k], h16, l16);
+            sh[m] = __builtin_fmaf((float)h16, wf, sh[m]);
+            sl[m] = __builtin_fmaf((float)l16, wf, sl[m]);
+        }
+    }
+#pragma unroll
+    for (int sft = 1; sft < 64; sft <<= 1)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            sh[m] += __shfl_xor(sh[m], sft, 64);
+            sl[m] += __shfl_xor(sl[m], sft, 64);
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float v = merge_value(sh[m], sl[m]);
+            if (bias) v = v + bias[n];
+            y[m * ldy + n] = v;
+        }
+    }
+}
+
+template <int MR>
+hipError_t launch_nk_generic(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                             int64_t N, int64_t K, hipStream_t stream, const float *bias)
+{
+    const int64_t blocks = (N + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    gemv_nk_generic_kernel<MR><<<dim3((unsigned)blocks), 256, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias, N, K);
+    return hipGetLastError();
 }
 
 int64_t tiles_of(int64_t N) { return (N + kTileN - 1) / kTileN; }
@@ -404,11 +548,12 @@ bool buffer_path_ok(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
 
 template <int MR>
 hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                          int64_t N, int64_t K, hipStream_t stream)
+                          int64_t N, int64_t K, hipStream_t stream, const float *bias)
 {
     const int64_t blocks = (N + kGenericNB - 1) / kGenericNB;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    gemv_generic_kernel<MR><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K);
+    gemv_generic_kernel<MR><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K,
+                                                                                    bias);
     return hipGetLastError();
 }
 
@@ -433,7 +578,8 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
 }
 
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                       int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream)
+                       int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
+                       const float *bias)
 {
     if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
     const GemvPlan p = gemv_plan(M, N, K);
@@ -441,25 +587,51 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
         (p.workspace_bytes == 0 || (part && part_bytes >= p.workspace_bytes))) {
         const int64_t blocks = tiles_of(N) * p.chunks;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N)};
+        GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), bias};
         gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.chunks == 1) return e;
         const int64_t outs = M * N;
         if ((outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks, (int)M,
-                                                                                     N, y, ldy);
+                                                                                     N, y, ldy, bias);
         return hipGetLastError();
     }
     switch (M) {
-    case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 3: return launch_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 4: return launch_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 5: return launch_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 6: return launch_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    case 7: return launch_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream);
-    default: return launch_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream);
+    case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 3: return launch_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 4: return launch_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 5: return launch_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 6: return launch_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 7: return launch_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    default: return launch_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    }
+}
+
+hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias)
+{
+    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    constexpr int64_t kLimit = kNoOffset - (1 << 20);
+    const bool fast = K > 0 && K % 8 == 0 && ldw % 8 == 0 && ldx % 4 == 0 &&
+                      ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
+                      N * ldw * 2 < kLimit && M * ldx * 4 < kLimit && K < kLimit / 64;
+    if (fast) {
+        const int64_t blocks = (N + 63) / 64;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        gemv_nk_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias, (int)M, N, K);
+        return hipGetLastError();
+    }
+    switch (M) {
+    case 1: return launch_nk_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 2: return launch_nk_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 3: return launch_nk_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 4: return launch_nk_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 5: return launch_nk_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 6: return launch_nk_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 7: return launch_nk_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    default: return launch_nk_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
     }
 }
 

@@ -17,10 +17,14 @@ hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float
                         int64_t rows, int64_t cols, hipStream_t stream);
 
 // y (ldy) and/or c_hi, c_lo (ldc) outputs; any of them may be null.
+// bias (FP32 [N], or null): every launcher that writes y adds bias[n] to the
+// merged value, as one more FP32 addition (c_hi, c_lo stay the bare products).
+// w_nk: W is given as [N, K] (ldw >= K) instead of [K, N] (ldw >= N).
 // a_zero_padded: A's columns from K to the next multiple of 8 hold +0.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
+                       int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
+                       const float *bias = nullptr, bool w_nk = false);
 
 // Separate-addition accumulation mode: k_steps_per_add is 0 (plain
 // accumulation, same tile configuration), 1, 4 or 16 sixteen-deep k-steps per
@@ -33,15 +37,21 @@ hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, 
 // when the operands do not allow it, in which case nothing was enqueued.
 hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
-                           int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream);
+                           int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
+                           const float *bias = nullptr, bool w_nk = false);
 
 // LDS-DMA GEMM on FP32 A, split in registers (one launch for the whole
 // projection); hipErrorNotSupported, with nothing enqueued, unless K % 4 == 0,
 // lda % 4 == 0, ldw % 8 == 0 and A, W are 16-byte aligned.
 hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w, int64_t ldw, float *y,
-                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                                 const float *bias = nullptr, bool w_nk = false);
 
 constexpr int64_t kGemvMaxRows = 8;
+
+// Small-M path for W given as [N, K] (ldw >= K): one dispatch, no workspace.
+hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias = nullptr);
 
 // Small-M (1 <= M <= 8) path: K is cut into `chunks` row chunks of whole
 // stages (`stages` = ceil(K / 32) in all); with chunks > 1 the product
@@ -63,6 +73,6 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K);
 // fused generic kernel runs instead and `part` is not touched.
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
                        int64_t ldy, int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes,
-                       hipStream_t stream);
+                       hipStream_t stream, const float *bias = nullptr);
 
 }  // namespace cfp32

@@ -168,6 +168,34 @@ CFP32_API cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t 
                           float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Weight layouts for cfp32_linear_ex. */
+typedef enum {
+    CFP32_W_KN = 0, /* w is [K, N], row-major (the layout cfp32_linear takes) */
+    CFP32_W_NK = 1  /* w is [N, K], row-major: a torch.nn.Linear weight */
+} cfp32_w_layout;
+
+/* Workspace bytes cfp32_linear_ex needs for this shape and weight layout
+ * (0 when none is needed; 0 for negative sizes or an unknown layout). */
+CFP32_API size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K, int w_layout);
+
+/* The projection with the operations next to it in a model layer (guide:
+ * graph paragraph; small projections at their real batch size):
+ *   y = x W (+ bias), W in either layout.
+ *   x        : FP32 [M, K], leading dimension ldx >= K.
+ *   w        : FP16 bits; CFP32_W_KN: [K, N] with ldw >= N;
+ *              CFP32_W_NK: [N, K] with ldw >= K.
+ *   bias     : FP32 [N] or NULL; added to each merged output as one more
+ *              FP32 addition: y = fl32(merge(C_hi, C_lo) + bias[n]).
+ *   y        : FP32 [M, N], leading dimension ldy >= N.
+ *   workspace, workspace_bytes : as for cfp32_linear, sized by
+ *              cfp32_linear_ex_workspace_bytes(M, N, K, w_layout).
+ * With CFP32_W_KN and no bias this is exactly cfp32_linear (same kernels,
+ * same bits); without the bias, y equals the bias-free call to the bit.
+ * Unknown layouts give CFP32_ERR_INVALID_VALUE. */
+CFP32_API cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int w_layout,
+                             const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,6 +77,10 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
         assert need > 0
         assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, None, 0, None) == E
         assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, FAKE, need - 1, None) == E
+    # linear_ex: unknown layout; [N, K] weights need ldw >= K
+    assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 64, 2, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
+    assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 63, cf.W_NK, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
+    assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 32, cf.W_NK, None, FAKE, 64, 2, 16, 64, None, 0, None) == E
     # sizes whose extent overflows 64-bit offsets
     big = 1 << 40
     assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
@@ -97,6 +101,14 @@ def test_workspace_sizes(lib):
     # M=3, N=1000 (2 tiles), K=777: 128 chunks wanted, ceil(777 / 32) = 25 stages.
     assert cf.cfp32_linear_workspace_bytes(3, 1000, 777) == 25 * 3 * 2 * 1024 * 4 + 256
     assert cf.cfp32_linear_workspace_bytes(8, 4096, 0) == 0
+    # cfp32_linear_ex: [K, N] as cfp32_linear; [N, K] needs nothing for M <= 8
+    # (one dispatch) and the hi/lo planes above; unknown layouts give 0.
+    for shape in [(1, 14336, 4096), (8, 4096, 4096), (3, 1000, 777), (4096, 4096, 4096), (9, 5, 1)]:
+        assert cf.cfp32_linear_ex_workspace_bytes(*shape, cf.W_KN) == cf.cfp32_linear_workspace_bytes(*shape)
+    assert cf.cfp32_linear_ex_workspace_bytes(1, 14336, 4096, cf.W_NK) == 0
+    assert cf.cfp32_linear_ex_workspace_bytes(8, 4096, 4096, cf.W_NK) == 0
+    assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, cf.W_NK) == 2 * 256 + 256
+    assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, 7) == 0
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(-1, 10, 10) == 0

@@ -272,6 +272,15 @@ def main():
         b.synchronize()
         return a.elapsed_time(b) / n * 1e3
 
+    # The decode projection with the weights as torch.nn.Linear stores them
+    # ([N, K]): one dispatch, each output column streaming its own W row.
+    Wts = [Ws[0].view(K_, N_).t().contiguous()]
+    for _ in range(3):
+        Wts.append(Wts[0].clone())
+    gemv_nk_us = timed(lambda i: check(cf.cfp32_linear_ex(x1.data_ptr(), K_, Wts[i % 4].data_ptr(), K_, cf.W_NK,
+                                                          None, y1.data_ptr(), N_, M_DEC, N_, K_, None, 0, sh),
+                                       "decode nk"), 100)
+    del Wts
     gemv_us = timed(lambda i: check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y1.data_ptr(), N_,
                                                     M_DEC, N_, K_, dec_ws.data_ptr(), dec_ws_bytes, sh), "decode"), 100)
     sq = workloads.square()
@@ -348,6 +357,8 @@ def main():
             "gemv_1x4096x14336_us": round(gemv_us, 2),
             "gemv_GBps": round(dec_bytes / (gemv_us * 1e-6) / 1e9, 1),
             "gemv_frac_hbm": round(dec_bytes / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemv_nk_1x4096x14336_us": round(gemv_nk_us, 2),
+            "gemv_nk_frac_hbm": round(dec_bytes / (gemv_nk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
         "fp32_ab_4096": {
             "cfp32_linear_us": round(lin_us, 2),

@@ -24,6 +24,8 @@ Functions (arrays are numpy; FP16 travels as uint16 bit patterns):
 * ``y64``                      -- O5(a), FP64 reference and sum |a w| for a
                                   whole output, via a float64 matmul.
 * ``y64_at``, ``ideal64_at``   -- O5(a)/(e) at chosen output positions.
+* ``gelu64``, ``geglu64``      -- the GEGLU step after an FFN projection
+                                  (exact GELU, g * Phi(g)), in double.
 
 Pins (what this oracle is checked against, apart from itself) live in
 ``tests/test_oracle_*.py``.
@@ -93,6 +95,10 @@ def _load():
     lib.o_dot64_at.restype = None
     lib.o_ideal64_at.argtypes = [P, I64, P, I64, I64, P, P, I64, P]
     lib.o_ideal64_at.restype = None
+    lib.o_gelu64.argtypes = [ctypes.c_double]
+    lib.o_gelu64.restype = ctypes.c_double
+    lib.o_geglu64.argtypes = [P, P, I64, P]
+    lib.o_geglu64.restype = None
     if not lib.o_fp_env_ok():
         raise RuntimeError("oracle: host FP environment has FTZ/DAZ or a non-nearest rounding mode")
     _lib = lib
@@ -252,4 +258,23 @@ def ideal64_at(A, W, rows, cols):
     out = np.empty(rows.size, np.float64)
     _load().o_ideal64_at(_ptr(A), A.shape[1], _ptr(W), W.shape[1], A.shape[1], _ptr(rows),
                          _ptr(cols), rows.size, _ptr(out))
+    return out
+
+
+def gelu64(g) -> np.ndarray:
+    """gelu(g) = g/2 (1 + erf(g / sqrt 2)) in double, elementwise."""
+    lib = _load()
+    g = np.asarray(g, np.float64)
+    return np.vectorize(lib.o_gelu64, otypes=[np.float64])(g) if g.size else g.copy()
+
+
+def geglu64(gate, up) -> np.ndarray:
+    """gelu(gate) * up in double from FP32 gate and up of one shape."""
+    lib = _load()
+    gate = _c(gate, np.float32)
+    up = _c(up, np.float32)
+    if gate.shape != up.shape:
+        raise ValueError("gate and up differ in shape")
+    out = np.empty(gate.shape, np.float64)
+    lib.o_geglu64(_ptr(gate), _ptr(up), gate.size, _ptr(out))
     return out

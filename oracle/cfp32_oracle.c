@@ -325,3 +325,19 @@ void o_ideal64_at(const float *A, int64_t lda, const uint16_t *W, int64_t ldw,
         out[t] = s;
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* GEGLU (laya.cpp Vulkan guide, graph paragraph: the FP32 feed-forward      */
+/* layers apply GEGLU to the projection output in one fused step).  The      */
+/* guide names no GELU approximation; the exact form x * Phi(x) is used:     */
+/*   gelu(g) = g / 2 * (1 + erf(g / sqrt 2)),  out = gelu(gate) * up,        */
+/* in double precision from the FP32 gate and up values.                     */
+/* ------------------------------------------------------------------------- */
+
+double o_gelu64(double g) { return 0.5 * g * (1.0 + erf(g / sqrt(2.0))); }
+
+void o_geglu64(const float *gate, const float *up, int64_t n, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = o_gelu64((double)gate[i]) * (double)up[i];
+}

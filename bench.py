@@ -22,6 +22,8 @@ One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
 ``headline`` (the 4096^3 GEMM and the M = 1 decode path measured on their
 own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
 the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
+``geglu_ffn_8192x4096x7168`` (the FFN projection with its GEGLU fused,
+next to the plain projection of the same operands),
 ``separate_add_4096`` (the separate-addition accumulation mode at 4096^3,
 k_per_add 0 = plain accumulation in the same kernel configuration),
 ``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded sample
@@ -305,6 +307,19 @@ def main():
     yf32 = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
     fp32_us = timed(lambda i: torch.matmul(xs, wf32, out=yf32), 20)
     del lin_ws, wf32, yf32
+    # The FFN projection with its GEGLU fused (x2 [8192, 4096], W [4096, 14336]
+    # as gate | up, F = 7168) next to the plain projection of the same operands.
+    geglu_ws_bytes = cf.cfp32_linear_geglu_workspace_bytes(M_PRE, N_ // 2, K_)
+    geglu_ws = torch.empty(geglu_ws_bytes, dtype=torch.uint8, device=dev)
+    geglu_out = torch.empty((M_PRE, N_ // 2), dtype=torch.float32, device=dev)
+    geglu_us = timed(lambda i: check(cf.cfp32_linear_geglu(x2.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, None,
+                                                           geglu_out.data_ptr(), N_ // 2, M_PRE, N_ // 2, K_,
+                                                           geglu_ws.data_ptr(), geglu_ws_bytes, sh),
+                                     "geglu"), 10)
+    plain_us = timed(lambda i: check(cf.cfp32_linear(x2.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y2.data_ptr(), N_,
+                                                     M_PRE, N_, K_, geglu_ws.data_ptr(), geglu_ws_bytes, sh),
+                                     "linear"), 10)
+    del geglu_ws, geglu_out
     # The separate-addition accumulation mode at 4096^3 (same split planes),
     # with plain accumulation in the same kernel configuration as its baseline.
     sep_us = {}
@@ -366,6 +381,11 @@ def main():
             "fp32_library_matmul_us": round(fp32_us, 2),
             "fp32_library_tflops": round(2 * 4096 ** 3 / (fp32_us * 1e-6) / 1e12, 1),
             "speedup": round(fp32_us / lin_us, 2),
+        },
+        "geglu_ffn_8192x4096x7168": {
+            "linear_geglu_us": round(geglu_us, 2),
+            "linear_plain_us": round(plain_us, 2),
+            "geglu_tflops_fp32eq": round(2 * M_PRE * N_ * K_ / (geglu_us * 1e-6) / 1e12, 1),
         },
         "separate_add_4096": {
             "gemm_us": round(sq_us, 2),

@@ -10,7 +10,8 @@ pointers, sizes, stream handle):
 
     cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
     cfp32_linear, cfp32_linear_workspace_bytes, cfp32_linear_ex,
-    cfp32_linear_ex_workspace_bytes, cfp32_status_string, cfp32_last_hip_error
+    cfp32_linear_ex_workspace_bytes, cfp32_linear_geglu,
+    cfp32_linear_geglu_workspace_bytes, cfp32_status_string, cfp32_last_hip_error
 
 Tensor-level helpers (``split``, ``gemm``, ``merge``, ``linear``) check dtype,
 device and layout, pass ``data_ptr()`` and the current stream, and raise
@@ -38,6 +39,8 @@ EXPORTS = (
     "cfp32_linear",
     "cfp32_linear_ex_workspace_bytes",
     "cfp32_linear_ex",
+    "cfp32_linear_geglu_workspace_bytes",
+    "cfp32_linear_geglu",
 )
 
 W_KN, W_NK = 0, 1
@@ -85,6 +88,10 @@ def load_library():
     lib.cfp32_linear_ex_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear_ex.argtypes = [P, I64, P, I64, I32, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.cfp32_linear_ex.restype = I32
+    lib.cfp32_linear_geglu_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.cfp32_linear_geglu_workspace_bytes.restype = ctypes.c_size_t
+    lib.cfp32_linear_geglu.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.cfp32_linear_geglu.restype = I32
     _lib = lib
     return lib
 
@@ -131,6 +138,15 @@ def cfp32_linear_ex_workspace_bytes(M, N, K, w_layout) -> int:
 def cfp32_linear_ex(x, ldx, w, ldw, w_layout, bias, y, ldy, M, N, K, workspace, workspace_bytes, stream) -> int:
     return int(load_library().cfp32_linear_ex(x, ldx, w, ldw, w_layout, bias, y, ldy, M, N, K, workspace,
                                               workspace_bytes, stream))
+
+
+def cfp32_linear_geglu_workspace_bytes(M, F, K) -> int:
+    return int(load_library().cfp32_linear_geglu_workspace_bytes(M, F, K))
+
+
+def cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace, workspace_bytes, stream) -> int:
+    return int(load_library().cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace,
+                                                 workspace_bytes, stream))
 
 
 # -- tensor helpers -------------------------------------------------------------
@@ -279,4 +295,32 @@ def linear(x, w, out=None, workspace: Workspace | None = None, stream=None, bias
     pws = ws.data_ptr() if ws is not None else None
     _check(cfp32_linear_ex(px, ldx, pw, ldw, layout, pb, py, ldy, M, N, K, pws, need, _stream(stream)),
            "cfp32_linear_ex")
+    return out
+
+
+def linear_geglu(x, w, bias=None, out=None, workspace: Workspace | None = None, stream=None):
+    """out = gelu(x W[:, :F] + b[:F]) * (x W[:, F:] + b[F:]): x FP32 [M,K], w FP16
+    [K, 2F] (gate columns, then up columns), bias FP32 [2F] or None."""
+    torch = _torch()
+    px, M, K, ldx = _mat(x, (torch.float32,), "x")
+    pw, K2, N2, ldw = _mat(w, _f16_dtypes(), "w")
+    if K2 != K or N2 % 2:
+        raise ValueError("w must be [K, 2F]")
+    F = N2 // 2
+    pb = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.device != x.device or bias.dim() != 1 or bias.shape[0] != 2 * F \
+                or (F > 0 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous FP32 [2F] tensor on x's device")
+        pb = bias.data_ptr()
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=x.device)
+    po, M3, F3, ldo = _mat(out, (torch.float32,), "out")
+    if (M3, F3) != (M, F):
+        raise ValueError("out has the wrong shape")
+    need = cfp32_linear_geglu_workspace_bytes(M, F, K)
+    ws = (workspace or _default_ws).get(need, x.device)
+    pws = ws.data_ptr() if ws is not None else None
+    _check(cfp32_linear_geglu(px, ldx, pw, ldw, pb, po, ldo, M, F, K, pws, need, _stream(stream)),
+           "cfp32_linear_geglu")
     return out

@@ -41,6 +41,16 @@ __device__ __forceinline__ float merge_value(float c_hi, float c_lo)
     return c_hi + t;
 }
 
+// GELU in its exact form, x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)), in FP32
+// (the GEGLU activation of the laya.cpp Vulkan guide's graph paragraph, which
+// names the fused GEGLU shader but not a GELU approximation).
+__device__ __forceinline__ float gelu_value(float x)
+{
+    const float t = x * 0.70710678118654752f;
+    const float c = 1.0f + erff(t);
+    return (0.5f * x) * c;
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);

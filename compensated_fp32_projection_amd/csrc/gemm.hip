@@ -80,6 +80,7 @@ struct GemmArgs {
     int64_t ldc;
     int64_t M, N, K;
     const float *bias;  // FP32 [N] added to y after the merge, or null
+    int geglu_rmw;      // y holds a GEGLU gate on entry: y = gelu(y) * (merged value + bias)
 };
 
 // Slot of A granule (k-group kg, tile row `row`) of plane p inside a stage.
@@ -415,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
                 if (g.y) {
                     float v = merge_value(h, l);
                     if (g.bias) v = v + g.bias[col];
+                    if (g.geglu_rmw) v = gelu_value(g.y[row * g.ldy + col]) * v;
                     g.y[row * g.ldy + col] = v;
                 }
                 if (g.c_hi) {
@@ -467,11 +469,11 @@ int64_t tiles_of(int64_t M, int64_t N)
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
-                       const float *bias, bool w_nk)
+                       const float *bias, bool w_nk, bool geglu_rmw)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias, geglu_rmw ? 1 : 0};
     constexpr int64_t kCus = 256;
-    if (tiles_of<TileLarge>(M, N) >= kCus) {
+    if (tiles_of<TileLarge>(M, N) >= kCus && !geglu_rmw) {
         const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
                                              a_zero_padded, stream, bias, w_nk);
         if (e != hipErrorNotSupported) return e;
@@ -490,7 +492,7 @@ hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, 
                                     int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                                     int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr, 0};
     switch (k_steps_per_add) {
     case 0: return launch_tile<TileMedium, 0>(g, stream);
     case 1: return launch_tile<TileMedium, 1>(g, stream);

@@ -137,6 +137,7 @@ struct DmaArgs {
     int64_t M, N, K;
     int64_t Ka;  // columns of A that may be read: K, or K rounded up to 8 when A is zero-padded
     const float *bias;  // FP32 [N] added to y after the merge, or null
+    int64_t F;          // GEGLU variant: output columns; W, bias are [.., 2F] (gate | up)
 };
 
 // FP32 A in LDS (SPLIT variant): each 128-byte row of 32 floats is 8
@@ -155,7 +156,16 @@ __device__ __forceinline__ int a32_slot(int row, int g) { return row * 8 + (g ^ 
 // are loaded and converted by group g's own waves only, so the barriers that
 // already separate the two groups' phases order every conversion.
 // WNK = true: W is [N, K] (ldw >= K, K % 8 == 0), else [K, N].
-template <bool SPLIT, bool WNK>
+//
+// GEGLU = true (with [K, N] W, N = 2F): the feed-forward GEGLU of the laya.cpp
+// Vulkan guide's graph paragraph fused into the epilogue, out = gelu(gate) *
+// up with gate = x W[:, :F] and up = x W[:, F:].  A block computes 128
+// output columns: wave column wn owns output columns 32 wn .. 32 wn + 31 and
+// multiplies their gate columns in its first 32x32 block and their up
+// columns in its second, so one lane holds the gate and up of the same
+// output and applies the activation there.  Products, k order and merge are
+// those of the plain GEMM.
+template <bool SPLIT, bool WNK, bool GEGLU = false>
 __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
     const int tid = threadIdx.x;
@@ -166,11 +176,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int wn = wave % WAVES_N;
 
     const int64_t nbm = (g.M + BM - 1) / BM;
-    const int64_t nbn = (g.N + BN - 1) / BN;
+    static_assert(!GEGLU || (TN == 2 && !WNK && !SPLIT), "GEGLU: two 32-column blocks per wave, [K, N] W");
+    constexpr int TW = GEGLU ? BN / 2 : BN;  // output columns per block
+    const int64_t ncols = GEGLU ? g.F : g.N;
+    const int64_t nbn = (ncols + TW - 1) / TW;
     int64_t tile_m, tile_n;
     tile_of_block(blockIdx.x, nbm, nbn, tile_m, tile_n);
     const int64_t m0 = tile_m * BM;
-    const int64_t n0 = tile_n * BN;
+    const int64_t n0 = tile_n * TW;
 
     // SPLIT: both A resources cover the FP32 matrix (rs_lo is unused).
     const __amdgpu_buffer_rsrc_t rs_hi =
@@ -223,8 +236,18 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         } else {
             const int k = slot / WG;
             const int ng = (slot % WG) ^ ((k & 3) << 2);
-            const bool ok = n0 + 8 * ng < g.N;
-            w_off[jj] = ok ? (int)((k * g.ldw + n0 + 8 * ng) * 2) : kNoOffset;
+            int64_t gcol;  // W column of this granule's first of 8 columns
+            bool ok;
+            if constexpr (GEGLU) {
+                const int c = 8 * ng;  // tile column: wave column c / 64, block (c / 32) % 2
+                const int64_t out_col = n0 + 32 * (c >> 6) + (c & 31);
+                ok = out_col < g.F;
+                gcol = out_col + (((c >> 5) & 1) ? g.F : 0);
+            } else {
+                gcol = n0 + 8 * ng;
+                ok = gcol < g.N;
+            }
+            w_off[jj] = ok ? (int)((k * g.ldw + gcol) * 2) : kNoOffset;
             w_kend[jj] = ok ? (int)(g.K - k) : 0;
         }
     }
@@ -380,6 +403,25 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 
     // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31);
     // element e holds row 8*(e/4) + 4*(lane/32) + (e%4) of the block.
+    if constexpr (GEGLU) {
+        const int64_t col = n0 + 32 * wn + (lane & 31);
+        if (col >= g.F) return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row >= g.M) continue;
+                float gate = merge_value(acc_hi[i][0][e], acc_lo[i][0][e]);
+                float up = merge_value(acc_hi[i][1][e], acc_lo[i][1][e]);
+                if (g.bias) {
+                    gate = gate + g.bias[col];
+                    up = up + g.bias[g.F + col];
+                }
+                __builtin_nontemporal_store(gelu_value(gate) * up, g.y + row * g.ldy + col);
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -436,7 +478,7 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
     if ((M + BM) * lda * 2 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias};
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias, 0};
     if (w_nk)
         gemm_dma_kernel<false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
@@ -459,11 +501,31 @@ hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w,
     if ((M + BM) * lda * 4 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K, bias};
+    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K, bias, 0};
     if (w_nk)
         gemm_dma_kernel<true, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
         gemm_dma_kernel<true, false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
+// GEGLU-fused GEMM on the split planes: out [M, F] = gelu(x W[:, :F] + b[:F])
+// * (x W[:, F:] + b[F:]), W [K, 2F] (ldw >= 2F), bias [2F] or null.  Same
+// operand conditions as launch_gemm_dma; hipErrorNotSupported otherwise.
+hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                                 int64_t ldw, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
+                                 bool a_zero_padded, hipStream_t stream, const float *bias)
+{
+    if (K <= 0 || lda % 8 || ldw % 8 || !aligned16(a_hi) || !aligned16(a_lo) || !aligned16(w))
+        return hipErrorNotSupported;
+    const int64_t Ka = (K % 8 == 0) ? K : (a_zero_padded ? (K + 7) / 8 * 8 : -1);
+    if (Ka < 0 || Ka > lda) return hipErrorNotSupported;
+    constexpr int64_t kLim = kNoOffset - (1 << 20);
+    if ((M + BM) * lda * 2 >= kLim || !w_fits(ldw, 2 * F, K, false)) return hipErrorNotSupported;
+    const int64_t blocks = ((M + BM - 1) / BM) * ((F + BN / 2 - 1) / (BN / 2));
+    if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, out, ldo, nullptr, nullptr, ldo, M, 2 * F, K, Ka, bias, F};
+    gemm_dma_kernel<false, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();
 }
 

@@ -118,6 +118,7 @@ struct GemvArgs {
     int64_t chunks;   // the stages split as evenly as possible, in order
     int64_t ntiles;   // ceil(N / 512)
     const float *bias;  // FP32 [N] added to y after the merge, or null
+    int geglu;          // partial sums always (a GEGLU merge follows), never y
 };
 
 __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
         for (int t = 0; t < 8; ++t) {
             const int64_t n = col0 + 16 * t;
             const float ch = acc[t][2 * q], cl = acc[t][2 * q + 1];
-            if (g.chunks == 1) {
+            if (g.chunks == 1 && !g.geglu) {
                 if (n < g.N) {
                     float v = merge_value(ch, cl);
                     if (g.bias) v = v + g.bias[n];
@@ -318,6 +319,47 @@ __global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict
     __builtin_nontemporal_store(v, y + m * ldy + n);
 }
 
+// GEGLU merge (the laya.cpp Vulkan guide's fused GEGLU step, graph
+// paragraph): for output (m, n < F), the chunk sums of columns n (gate) and
+// F + n (up) in chunk order, each merged (plus its bias), then
+// out = gelu(gate) * up.
+__global__ __launch_bounds__(256) void gemv_geglu_merge_kernel(const float *__restrict__ part, int64_t n_pad,
+                                                               int64_t chunks, int M, int64_t F,
+                                                               float *__restrict__ y, int64_t ldy,
+                                                               const float *__restrict__ bias)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * F) return;
+    const int m = (int)(i / F);
+    const int64_t n = i % F;
+    const int64_t stride = (int64_t)M * 2 * n_pad;
+    float v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // h = 0: gate column n, h = 1: up column F + n
+        const float *p = part + (int64_t)m * 2 * n_pad + n + h * F;
+        float th = 0.0f, tl = 0.0f;
+        for (int64_t c0 = 0; c0 < chunks; c0 += kMergeBatch) {
+            float vh[kMergeBatch], vl[kMergeBatch];
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const bool in = c0 + j < chunks;
+                vh[j] = in ? __builtin_nontemporal_load(p + (c0 + j) * stride) : 0.0f;
+                vl[j] = in ? __builtin_nontemporal_load(p + (c0 + j) * stride + n_pad) : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {
+                if (c0 + j < chunks) {
+                    th += vh[j];
+                    tl += vl[j];
+                }
+            }
+        }
+        v[h] = merge_value(th, tl);
+        if (bias) v[h] = v[h] + bias[n + h * F];
+    }
+    __builtin_nontemporal_store(gelu_value(v[0]) * v[1], y + m * ldy + n);
+}
+
 // Fallback for W that is not 16-byte aligned or too large for 32-bit buffer
 // offsets: a block per 64 columns and all of K, element loads, the same
 // fixed-order reduction inside the block, one launch, no workspace.
@@ -329,7 +371,7 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
                                                                        const uint16_t *__restrict__ w, int64_t ldw,
                                                                        float *__restrict__ y, int64_t ldy,
                                                                        int64_t N, int64_t K,
-                                                                       const float *__restrict__ bias)
+                                                                       const float *__restrict__ bias, int geglu_rmw)
 {
     constexpr int CH = kGenericNB / 8;
     constexpr int KL = kGenericThreads / CH;
@@ -399,6 +441,7 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
         }
         float v = merge_value(th, tl);
         if (bias) v = v + bias[gn];
+        if (geglu_rmw) v = gelu_value(y[m * ldy + gn]) * v;  // y held the GEGLU gate
         y[m * ldy + gn] = v;
     }
 }
@@ -548,12 +591,12 @@ bool buffer_path_ok(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
 
 template <int MR>
 hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
-                          int64_t N, int64_t K, hipStream_t stream, const float *bias)
+                          int64_t N, int64_t K, hipStream_t stream, const float *bias, bool geglu_rmw)
 {
     const int64_t blocks = (N + kGenericNB - 1) / kGenericNB;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     gemv_generic_kernel<MR><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K,
-                                                                                    bias);
+                                                                                    bias, geglu_rmw ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -579,15 +622,15 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
 
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                        int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
-                       const float *bias)
+                       const float *bias, bool geglu_rmw)
 {
     if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
     const GemvPlan p = gemv_plan(M, N, K);
-    if (p.chunks > 0 && buffer_path_ok(x, ldx, w, ldw, M, K) &&
+    if (!geglu_rmw && p.chunks > 0 && buffer_path_ok(x, ldx, w, ldw, M, K) &&
         (p.workspace_bytes == 0 || (part && part_bytes >= p.workspace_bytes))) {
         const int64_t blocks = tiles_of(N) * p.chunks;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), bias};
+        GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), bias, 0};
         gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || p.chunks == 1) return e;
@@ -598,15 +641,46 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
         return hipGetLastError();
     }
     switch (M) {
-    case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 3: return launch_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 4: return launch_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 5: return launch_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 6: return launch_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    case 7: return launch_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
-    default: return launch_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
+    case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 3: return launch_generic<3>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 4: return launch_generic<4>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 5: return launch_generic<5>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 6: return launch_generic<6>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    case 7: return launch_generic<7>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
+    default: return launch_generic<8>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
     }
+}
+
+// GEGLU for 1 <= M <= 8: the product dispatch over all 2F columns of W
+// [K, 2F] (partial sums always, even for a single chunk), then the GEGLU
+// merge.  hipErrorNotSupported (nothing enqueued) when W does not allow the
+// buffer path or `part` is missing or too small.
+GemvPlan gemv_geglu_plan(int64_t M, int64_t F, int64_t K)
+{
+    GemvPlan p = gemv_plan(M, 2 * F, K);
+    if (p.chunks > 0) p.workspace_bytes = (size_t)p.chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *out, int64_t ldo,
+                             int64_t M, int64_t F, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
+                             const float *bias)
+{
+    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    const GemvPlan p = gemv_geglu_plan(M, F, K);
+    if (p.chunks == 0 || !buffer_path_ok(x, ldx, w, ldw, M, K) || !part || part_bytes < p.workspace_bytes)
+        return hipErrorNotSupported;
+    const int64_t N = 2 * F;
+    const int64_t blocks = tiles_of(N) * p.chunks;
+    if (blocks > 0x7FFFFFFF || (M * F + 255) / 256 > 0x7FFFFFFF) return hipErrorNotSupported;
+    GemvArgs g{x, ldx, w, ldw, part, nullptr, 0, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), nullptr, 1};
+    gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    gemv_geglu_merge_kernel<<<dim3((unsigned)((M * F + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks,
+                                                                                        (int)M, F, out, ldo, bias);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,

@@ -20,11 +20,13 @@ hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float
 // bias (FP32 [N], or null): every launcher that writes y adds bias[n] to the
 // merged value, as one more FP32 addition (c_hi, c_lo stay the bare products).
 // w_nk: W is given as [N, K] (ldw >= K) instead of [K, N] (ldw >= N).
+// geglu_rmw (launch_gemm, launch_gemv): y holds the GEGLU gate on entry and
+// receives gelu(gate) * (merged value + bias); runs the generic kernels.
 // a_zero_padded: A's columns from K to the next multiple of 8 hold +0.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
-                       const float *bias = nullptr, bool w_nk = false);
+                       const float *bias = nullptr, bool w_nk = false, bool geglu_rmw = false);
 
 // Separate-addition accumulation mode: k_steps_per_add is 0 (plain
 // accumulation, same tile configuration), 1, 4 or 16 sixteen-deep k-steps per
@@ -46,6 +48,12 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
 hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w, int64_t ldw, float *y,
                                  int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
                                  const float *bias = nullptr, bool w_nk = false);
+
+// GEGLU-fused GEMM on split planes (see gemm_dma.hip); hipErrorNotSupported,
+// with nothing enqueued, when the LDS-DMA conditions do not hold.
+hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                                 int64_t ldw, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
+                                 bool a_zero_padded, hipStream_t stream, const float *bias);
 
 constexpr int64_t kGemvMaxRows = 8;
 
@@ -73,6 +81,13 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K);
 // fused generic kernel runs instead and `part` is not touched.
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
                        int64_t ldy, int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes,
-                       hipStream_t stream, const float *bias = nullptr);
+                       hipStream_t stream, const float *bias = nullptr, bool geglu_rmw = false);
+
+// GEGLU for 1 <= M <= 8 over W [K, 2F]: out [M, F] = gelu(gate) * up.  The
+// plan's workspace holds partial sums for all 2F columns.
+GemvPlan gemv_geglu_plan(int64_t M, int64_t F, int64_t K);
+hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *out, int64_t ldo,
+                             int64_t M, int64_t F, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
+                             const float *bias);
 
 }  // namespace cfp32

@@ -196,6 +196,31 @@ CFP32_API cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16
                              const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes cfp32_linear_geglu needs (0 when none is needed). */
+CFP32_API size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_t K);
+
+/* The feed-forward projection with its GEGLU fused (guide: graph paragraph,
+ * the fused GEGLU shader of the FP32 feed-forward layers):
+ *   gate = x W[:, :F] (+ bias[:F]),  up = x W[:, F:] (+ bias[F:]),
+ *   out  = gelu(gate) * up,  gelu(g) = g * Phi(g) = g/2 (1 + erf(g / sqrt 2)).
+ *   x    : FP32 [M, K], ldx >= K.
+ *   w    : FP16 bits [K, 2F], ldw >= 2F: gate columns first, then up.
+ *   bias : FP32 [2F] or NULL.
+ *   out  : FP32 [M, F], ldo >= F.
+ *   workspace, workspace_bytes : as for cfp32_linear, sized by
+ *          cfp32_linear_geglu_workspace_bytes(M, F, K).
+ * gate and up are the projection's merged outputs (the same bits
+ * cfp32_linear gives for those columns); the activation and the product run
+ * in FP32 in the kernel that merges them (erff and three roundings).
+ * M > 8 with at least 256 output tiles of 128 x 128 (and aligned operands):
+ * the split, then one GEMM launch with the GEGLU in its epilogue.  M <= 8:
+ * the small-M product dispatch over all 2F columns, then a merge dispatch
+ * that forms out.  Other cases run the gate projection into out and the up
+ * projection with a read-modify-write epilogue (one more launch). */
+CFP32_API cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
+                                const float *bias, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

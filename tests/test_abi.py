@@ -81,6 +81,12 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 64, 2, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
     assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 63, cf.W_NK, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
     assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 32, cf.W_NK, None, FAKE, 64, 2, 16, 64, None, 0, None) == E
+    # linear_geglu: w narrower than 2F, out narrower than F, small workspace
+    assert cf.cfp32_linear_geglu(FAKE, 64, FAKE, 63, None, FAKE, 32, 2, 32, 64, None, 0, None) == E
+    assert cf.cfp32_linear_geglu(FAKE, 64, FAKE, 64, None, FAKE, 31, 2, 32, 64, None, 0, None) == E
+    need = cf.cfp32_linear_geglu_workspace_bytes(2, 32, 64)
+    assert need > 0
+    assert cf.cfp32_linear_geglu(FAKE, 64, FAKE, 64, None, FAKE, 32, 2, 32, 64, FAKE, need - 1, None) == E
     # sizes whose extent overflows 64-bit offsets
     big = 1 << 40
     assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
@@ -109,6 +115,12 @@ def test_workspace_sizes(lib):
     assert cf.cfp32_linear_ex_workspace_bytes(8, 4096, 4096, cf.W_NK) == 0
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, cf.W_NK) == 2 * 256 + 256
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, 7) == 0
+    # cfp32_linear_geglu: M <= 8 holds partial sums for all 2F columns, even
+    # for a single chunk; M > 8 the hi/lo planes.
+    assert cf.cfp32_linear_geglu_workspace_bytes(1, 7168, 4096) == 9 * 1 * 2 * 14336 * 4 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 8) == 1 * 2 * 2 * 512 * 4 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 2 * 256 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(-1, 10, 10) == 0
@@ -121,6 +133,8 @@ def test_empty_problems_are_no_ops(lib):
     assert cf.cfp32_split(None, 0, None, None, 0, 0, 5, None) == cf.OK
     assert cf.cfp32_gemm(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, None) == cf.OK
     assert cf.cfp32_gemm_separate_add(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, 64, None) == cf.OK
+    assert cf.cfp32_linear_geglu(None, 0, None, 0, None, None, 0, 0, 8, 8, None, 0, None) == cf.OK
+    assert cf.cfp32_linear_geglu(None, 0, None, 0, None, None, 0, 3, 0, 8, None, 0, None) == cf.OK
     assert cf.cfp32_merge(None, None, 0, None, 0, 4, 0, None) == cf.OK
     assert cf.cfp32_linear(None, 0, None, 0, None, 0, 0, 8, 8, None, 0, None) == cf.OK
 

@@ -50,7 +50,7 @@ PEAK_HBM_GBS = 8000.0
 K_, N_, M_DEC, M_PRE = 4096, 14336, 1, 8192
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_counters.txt")
 CALIB_BYTES = 512 * 1024 * 1024  # plain device copy of known size, for counter scaling
-GEMM_KERNEL = "gemm_dma_kernel"
+GEMM_KERNEL = "gemm_dma_kernel<false, false, false>"  # the plain [K, N] variant
 COPY_KERNEL_HINT = "copy"
 
 

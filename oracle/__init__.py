@@ -26,6 +26,8 @@ Functions (arrays are numpy; FP16 travels as uint16 bit patterns):
 * ``y64_at``, ``ideal64_at``   -- O5(a)/(e) at chosen output positions.
 * ``gelu64``, ``geglu64``      -- the GEGLU step after an FFN projection
                                   (exact GELU, g * Phi(g)), in double.
+* ``qkv_rotary``               -- Q/K/V packing with the rotary multiplication
+                                  after a QKV projection, in double.
 
 Pins (what this oracle is checked against, apart from itself) live in
 ``tests/test_oracle_*.py``.
@@ -99,6 +101,8 @@ def _load():
     lib.o_gelu64.restype = ctypes.c_double
     lib.o_geglu64.argtypes = [P, P, I64, P]
     lib.o_geglu64.restype = None
+    lib.o_qkv_rotary.argtypes = [P, I64, P, ctypes.c_double, I64, I64, I64, P, P, P]
+    lib.o_qkv_rotary.restype = None
     if not lib.o_fp_env_ok():
         raise RuntimeError("oracle: host FP environment has FTZ/DAZ or a non-nearest rounding mode")
     _lib = lib
@@ -278,3 +282,20 @@ def geglu64(gate, up) -> np.ndarray:
     out = np.empty(gate.shape, np.float64)
     lib.o_geglu64(_ptr(gate), _ptr(up), gate.size, _ptr(out))
     return out
+
+
+def qkv_rotary(qkv, H: int, D: int, pos=None, theta: float = 10000.0):
+    """(q, k, v), each float64 [H, T, D], from the FP32 QKV projection output
+    [T, 3 H D] (row t = [q | k | v], head h at h*D): q and k rotated in the
+    half-split pairing (d, d + D/2) by pos[t] * theta^(-2i/D); v copied."""
+    lib = _load()
+    qkv = _c(qkv, np.float32)
+    T = qkv.shape[0]
+    if qkv.shape[1] < 3 * H * D or D % 2:
+        raise ValueError("qkv must be [T, >= 3 H D] with D even")
+    pos = np.arange(T, dtype=np.int64) if pos is None else _c(pos, np.int64)
+    q = np.empty((H, T, D), np.float64)
+    k = np.empty((H, T, D), np.float64)
+    v = np.empty((H, T, D), np.float64)
+    lib.o_qkv_rotary(_ptr(qkv), qkv.shape[1], _ptr(pos), float(theta), T, H, D, _ptr(q), _ptr(k), _ptr(v))
+    return q, k, v

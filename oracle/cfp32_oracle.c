@@ -341,3 +341,38 @@ void o_geglu64(const float *gate, const float *up, int64_t n, double *out)
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = o_gelu64((double)gate[i]) * (double)up[i];
 }
+
+/* ------------------------------------------------------------------------- */
+/* Q/K/V packing with rotary multiplication (laya.cpp Vulkan guide, graph    */
+/* paragraph: one dispatch packs the projection output into Q, K and V and   */
+/* applies the rotary multiplication).  The guide gives no convention; the   */
+/* one taken here: row t of the projection output holds [q | k | v], each    */
+/* H heads of D values (head h at h*D); outputs are head-major [H][T][D];    */
+/* q and k are rotated in the half-split pairing, dims d and d + D/2 forming */
+/* pair i = d < D/2 with angle pos[t] * theta^(-2i/D):                       */
+/*   x1' = x1 cos - x2 sin,  x2' = x2 cos + x1 sin;  v is copied.             */
+/* Everything in double, from the FP32 inputs.                                */
+/* ------------------------------------------------------------------------- */
+
+void o_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *pos, double theta, int64_t T, int64_t H,
+                  int64_t D, double *q, double *k, double *v)
+{
+    const int64_t half = D / 2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t h = 0; h < H; ++h) {
+            const float *row = qkv + t * ldq;
+            for (int64_t i = 0; i < half; ++i) {
+                const double ang = (double)pos[t] * pow(theta, -2.0 * (double)i / (double)D);
+                const double c = cos(ang), s = sin(ang);
+                for (int p = 0; p < 2; ++p) {  /* p = 0: q, 1: k */
+                    const float *src = row + p * H * D + h * D;
+                    double *dst = (p == 0 ? q : k) + (h * T + t) * D;
+                    const double x1 = src[i], x2 = src[i + half];
+                    dst[i] = x1 * c - x2 * s;
+                    dst[i + half] = x2 * c + x1 * s;
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) v[(h * T + t) * D + d] = row[2 * H * D + h * D + d];
+        }
+}

@@ -11,7 +11,8 @@ pointers, sizes, stream handle):
     cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
     cfp32_linear, cfp32_linear_workspace_bytes, cfp32_linear_ex,
     cfp32_linear_ex_workspace_bytes, cfp32_linear_geglu,
-    cfp32_linear_geglu_workspace_bytes, cfp32_status_string, cfp32_last_hip_error
+    cfp32_linear_geglu_workspace_bytes, cfp32_qkv_rotary, cfp32_status_string,
+    cfp32_last_hip_error
 
 Tensor-level helpers (``split``, ``gemm``, ``merge``, ``linear``) check dtype,
 device and layout, pass ``data_ptr()`` and the current stream, and raise
@@ -41,6 +42,7 @@ EXPORTS = (
     "cfp32_linear_ex",
     "cfp32_linear_geglu_workspace_bytes",
     "cfp32_linear_geglu",
+    "cfp32_qkv_rotary",
 )
 
 W_KN, W_NK = 0, 1
@@ -92,6 +94,8 @@ def load_library():
     lib.cfp32_linear_geglu_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear_geglu.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.cfp32_linear_geglu.restype = I32
+    lib.cfp32_qkv_rotary.argtypes = [P, I64, P, ctypes.c_double, P, P, P, I64, I64, I64, P]
+    lib.cfp32_qkv_rotary.restype = I32
     _lib = lib
     return lib
 
@@ -147,6 +151,10 @@ def cfp32_linear_geglu_workspace_bytes(M, F, K) -> int:
 def cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace, workspace_bytes, stream) -> int:
     return int(load_library().cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace,
                                                  workspace_bytes, stream))
+
+
+def cfp32_qkv_rotary(qkv, ldq, positions, theta, q, k, v, T, H, D, stream) -> int:
+    return int(load_library().cfp32_qkv_rotary(qkv, ldq, positions, theta, q, k, v, T, H, D, stream))
 
 
 # -- tensor helpers -------------------------------------------------------------
@@ -324,3 +332,22 @@ def linear_geglu(x, w, bias=None, out=None, workspace: Workspace | None = None, 
     _check(cfp32_linear_geglu(px, ldx, pw, ldw, pb, po, ldo, M, F, K, pws, need, _stream(stream)),
            "cfp32_linear_geglu")
     return out
+
+
+def qkv_rotary(qkv, H: int, D: int, positions=None, theta: float = 10000.0, stream=None):
+    """(q, k, v), each FP32 [H, T, D], from a QKV projection output [T, 3 H D]
+    (row t = [q | k | v]); q and k rotated (half-split pairs), v copied."""
+    torch = _torch()
+    pq, T, C, ldq = _mat(qkv, (torch.float32,), "qkv")
+    if C < 3 * H * D:
+        raise ValueError("qkv has fewer than 3*H*D columns")
+    pp = None
+    if positions is not None:
+        if positions.dtype != torch.int64 or positions.device != qkv.device or positions.numel() != T \
+                or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int64 [T] tensor on qkv's device")
+        pp = positions.data_ptr()
+    q, k, v = (torch.empty((H, T, D), dtype=torch.float32, device=qkv.device) for _ in range(3))
+    _check(cfp32_qkv_rotary(pq, ldq, pp, float(theta), q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, D,
+                            _stream(stream)), "cfp32_qkv_rotary")
+    return q, k, v

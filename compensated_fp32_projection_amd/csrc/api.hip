@@ -303,4 +303,17 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
                                        bias_up, false, true));
 }
 
+cfp32_status cfp32_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *positions, double theta, float *q,
+                              float *k, float *v, int64_t T, int64_t H, int64_t D, void *stream)
+{
+    if (T < 0 || H < 0 || D < 0 || D % 2 || !(theta > 0.0)) return CFP32_ERR_INVALID_VALUE;
+    if (H > kMaxDim / 3 || (H > 0 && D > kMaxDim / (3 * H))) return CFP32_ERR_INVALID_VALUE;
+    if (T == 0 || H == 0 || D == 0) return CFP32_OK;
+    if (!qkv || !q || !k || !v || ldq < 3 * H * D || !extent_ok(T, ldq) || !extent_ok(T, H * D))
+        return CFP32_ERR_INVALID_VALUE;
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_qkv_rotary(qkv, ldq, positions, theta, q, k, v, T, H, D, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -55,6 +55,11 @@ hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int
                                  int64_t ldw, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                  bool a_zero_padded, hipStream_t stream, const float *bias);
 
+// Q/K/V packing + rotary (qkv_rotary.hip): qkv [T, >= 3HD] (ldq) -> q, k, v
+// [H][T][D]; pos (device, T entries) or null for 0 .. T-1; D even.
+hipError_t launch_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *pos, double theta, float *q, float *k,
+                             float *v, int64_t T, int64_t H, int64_t D, hipStream_t stream);
+
 constexpr int64_t kGemvMaxRows = 8;
 
 // Small-M path for W given as [N, K] (ldw >= K): one dispatch, no workspace.

@@ -221,6 +221,21 @@ CFP32_API cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uin
                                 const float *bias, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Q/K/V packing with the rotary multiplication, one dispatch (guide: graph
+ * paragraph), applied to a QKV projection's output.
+ *   qkv       : FP32 [T, 3*H*D] (ldq >= 3*H*D); row t = [q | k | v], each H
+ *               heads of D values, head h at h*D.
+ *   positions : int64 [T] device array of token positions, or NULL for
+ *               0 .. T-1.
+ *   theta     : rotary base (> 0), e.g. 10000.
+ *   q, k, v   : FP32 [H, T, D] each, contiguous (head-major).
+ *   D         : even.
+ * q and k are rotated in the half-split pairing: dims i and i + D/2 turn by
+ * pos * theta^(-2i/D), x1' = x1 cos - x2 sin, x2' = x2 cos + x1 sin; v is
+ * copied.  FP32 arithmetic (sincosf of the FP32 angle).  One kernel launch. */
+CFP32_API cfp32_status cfp32_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *positions, double theta,
+                              float *q, float *k, float *v, int64_t T, int64_t H, int64_t D, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

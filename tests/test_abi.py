@@ -87,6 +87,11 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     need = cf.cfp32_linear_geglu_workspace_bytes(2, 32, 64)
     assert need > 0
     assert cf.cfp32_linear_geglu(FAKE, 64, FAKE, 64, None, FAKE, 32, 2, 32, 64, FAKE, need - 1, None) == E
+    # qkv_rotary: odd D, non-positive theta, ldq below 3*H*D
+    assert cf.cfp32_qkv_rotary(FAKE, 96, None, 10000.0, FAKE, FAKE, FAKE, 4, 2, 15, None) == E
+    assert cf.cfp32_qkv_rotary(FAKE, 96, None, 0.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
+    assert cf.cfp32_qkv_rotary(FAKE, 95, None, 10000.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
+    assert cf.cfp32_qkv_rotary(None, 96, None, 10000.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
     # sizes whose extent overflows 64-bit offsets
     big = 1 << 40
     assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
@@ -134,6 +139,7 @@ def test_empty_problems_are_no_ops(lib):
     assert cf.cfp32_gemm(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, None) == cf.OK
     assert cf.cfp32_gemm_separate_add(None, None, 0, None, 0, None, None, None, 0, 0, 8, 8, 64, None) == cf.OK
     assert cf.cfp32_linear_geglu(None, 0, None, 0, None, None, 0, 0, 8, 8, None, 0, None) == cf.OK
+    assert cf.cfp32_qkv_rotary(None, 0, None, 10000.0, None, None, None, 0, 4, 8, None) == cf.OK
     assert cf.cfp32_linear_geglu(None, 0, None, 0, None, None, 0, 3, 0, 8, None, 0, None) == cf.OK
     assert cf.cfp32_merge(None, None, 0, None, 0, 4, 0, None) == cf.OK
     assert cf.cfp32_linear(None, 0, None, 0, None, 0, 0, 8, 8, None, 0, None) == cf.OK

@@ -280,6 +280,131 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
     }
 }
 
+// M <= 2: the same chunks and partial sums from the vector unit, which for
+// one or two rows streams W about a microsecond faster than the matrix-unit
+// kernel (its 16 waves per block keep more loads in flight; at M <= 2 the
+// FP32 FMAs cost little).  A block of 1024 threads owns one 512-column tile
+// of one chunk; wave v takes rows r0 + v, r0 + v + 16, ... and lane l columns
+// 8l .. 8l + 7, with 8 rows of loads (1 KiB each, streaming policy) in
+// flight; x is read with scalar loads (every lane needs the same value).
+// Products hi * w and lo * w accumulate with FP32 fused multiply-adds (the
+// FP16 x FP16 product is exact, so each step rounds once, as in the matrix
+// unit).  The 16 waves are summed in index order through LDS; the block then
+// writes its chunk's partial sums, or merges and writes y when K is one
+// chunk.
+constexpr int kValuThreads = 1024;
+constexpr int kValuU = 8;
+
+template <int MR>
+__global__ __launch_bounds__(kValuThreads) void gemv_valu_kernel(GemvArgs g)
+{
+    constexpr int WV = kValuThreads / 64;
+    __shared__ float red[WV][MR][2][kTileN];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned ntiles = (unsigned)g.ntiles;
+    const int tile = (int)(blockIdx.x % ntiles);
+    const int chunk = (int)(blockIdx.x / ntiles);
+    const int base = (int)(g.stages / g.chunks);
+    const int extra = (int)(g.stages % g.chunks);
+    const int s_begin = chunk * base + (chunk < extra ? chunk : extra);
+    const int ns = base + (chunk < extra ? 1 : 0);
+    const int64_t r0 = (int64_t)kBK * s_begin;
+    const int64_t r1 = (kBK * (int64_t)(s_begin + ns) < g.K) ? kBK * (int64_t)(s_begin + ns) : g.K;
+    const int64_t n0 = (int64_t)tile * kTileN;
+    const int64_t n = n0 + 8 * lane;
+
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)(g.K * g.ldw * 2), kBufferWord3);
+
+    float sh[MR][8], sl[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
+
+    for (int64_t kb = r0 + wave; kb < r1; kb += (int64_t)WV * kValuU) {
+        uint4 wv[kValuU];
+#pragma unroll
+        for (int u = 0; u < kValuU; ++u) {
+            const int64_t k = kb + (int64_t)u * WV;
+            const int off = (k < r1 && n < g.N) ? (int)((k * g.ldw + n) * 2) : kNoOffset;
+            wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, kStreamAux));
+        }
+        float xv[kValuU][MR];
+#pragma unroll
+        for (int u = 0; u < kValuU; ++u) {
+            const int64_t k = kb + (int64_t)u * WV;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) xv[u][m] = (k < r1) ? g.x[m * g.ldx + k] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kValuU; ++u) {
+            const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+            float wf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wf[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                _Float16 h16, l16;
+                split_value(xv[u][m], h16, l16);
+                const float h = (float)h16, l = (float)l16;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sh[m][e] = __builtin_fmaf(h, wf[e], sh[m][e]);
+                    sl[m][e] = __builtin_fmaf(l, wf[e], sl[m][e]);
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            red[wave][m][0][8 * lane + e] = sh[m][e];
+            red[wave][m][1][8 * lane + e] = sl[m][e];
+        }
+    __syncthreads();
+    // One thread per (row, column) of the tile: C_hi and C_lo, waves in order.
+    for (int o = threadIdx.x; o < MR * kTileN; o += kValuThreads) {
+        const int col = o % kTileN;
+        const int m = o / kTileN;
+        float th = 0.0f, tl = 0.0f;
+#pragma unroll
+        for (int v = 0; v < WV; ++v) {
+            th += red[v][m][0][col];
+            tl += red[v][m][1][col];
+        }
+        const int64_t nn = n0 + col;
+        if (g.chunks == 1 && !g.geglu) {
+            if (nn < g.N) {
+                float val = merge_value(th, tl);
+                if (g.bias) val = val + g.bias[nn];
+                __builtin_nontemporal_store(val, g.y + m * g.ldy + nn);
+            }
+        } else {
+            float *pp = g.part + ((chunk * g.M + m) * 2) * g.n_pad + nn;
+            __builtin_nontemporal_store(th, pp);
+            __builtin_nontemporal_store(tl, pp + g.n_pad);
+        }
+    }
+}
+
+// Product dispatch: the vector-unit kernel for M <= 2, the matrix-unit one above.
+hipError_t launch_product(const GemvArgs &g, int64_t blocks, hipStream_t stream)
+{
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (g.M == 1)
+        gemv_valu_kernel<1><<<dim3((unsigned)blocks), kValuThreads, 0, stream>>>(g);
+    else if (g.M == 2)
+        gemv_valu_kernel<2><<<dim3((unsigned)blocks), kValuThreads, 0, stream>>>(g);
+    else
+        gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    return hipGetLastError();
+}
+
 // y[m, n] = merge(sum over chunks of C_hi, sum over chunks of C_lo), chunks in
 // order.  The partial sums were written by blocks on every XCD, so they come
 // from memory, not from this XCD's L2: all loads of a batch of kMergeBatch
@@ -611,7 +736,15 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
     const int64_t ntiles = tiles_of(N);
     if (ntiles > ((int64_t)1 << 40)) return p;  // keeps the byte count below in range
     p.stages = (K + kBK - 1) / kBK;
+    // At most one block per CU; among those counts, the largest that deals the
+    // same number of blocks to each of the 8 XCDs (measured at 1 x 4096 x
+    // 14336: 8 chunks, 224 blocks, 0.4 us faster than 9 chunks, 252 blocks).
     int64_t chunks = kTargetBlocks / ntiles;
+    for (int64_t c = chunks; c >= 1 && c > chunks - 8; --c)
+        if ((c * ntiles) % 8 == 0) {
+            chunks = c;
+            break;
+        }
     if (chunks > p.stages) chunks = p.stages;
     if (chunks < 1) chunks = 1;
     p.chunks = chunks;
@@ -631,8 +764,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
         const int64_t blocks = tiles_of(N) * p.chunks;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), bias, 0};
-        gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_product(g, blocks, stream);
         if (e != hipSuccess || p.chunks == 1) return e;
         const int64_t outs = M * N;
         if ((outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
@@ -675,8 +807,7 @@ hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int
     const int64_t blocks = tiles_of(N) * p.chunks;
     if (blocks > 0x7FFFFFFF || (M * F + 255) / 256 > 0x7FFFFFFF) return hipErrorNotSupported;
     GemvArgs g{x, ldx, w, ldw, part, nullptr, 0, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), nullptr, 1};
-    gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_product(g, blocks, stream);
     if (e != hipSuccess) return e;
     gemv_geglu_merge_kernel<<<dim3((unsigned)((M * F + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks,
                                                                                         (int)M, F, out, ldo, bias);

@@ -99,10 +99,12 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
 
 def test_workspace_sizes(lib):
     # M <= 8: FP32 partial sums [chunks][M][2][N rounded up to 512] + 256 B
-    # slack.  512-column tiles, about 256 blocks over tiles x chunks, chunks of
-    # whole 32-row stages; a single chunk merges in place and needs nothing.
-    # M=1, N=14336 (28 tiles), K=4096: 256 // 28 = 9 chunks.
-    assert cf.cfp32_linear_workspace_bytes(1, 14336, 4096) == 9 * 1 * 2 * 14336 * 4 + 256
+    # slack.  512-column tiles, at most 256 blocks over tiles x chunks (the
+    # largest count within 8 of that which is a multiple of 8 blocks), chunks
+    # of whole 32-row stages; a single chunk merges in place and needs nothing.
+    # M=1, N=14336 (28 tiles), K=4096: 256 // 28 = 9, 9 * 28 = 252 is not a
+    # multiple of 8, 8 * 28 = 224 is: 8 chunks.
+    assert cf.cfp32_linear_workspace_bytes(1, 14336, 4096) == 8 * 1 * 2 * 14336 * 4 + 256
     # M=8, N=4096 (8 tiles): 32 chunks of 4 stages.
     assert cf.cfp32_linear_workspace_bytes(8, 4096, 4096) == 32 * 8 * 2 * 4096 * 4 + 256
     # M=1, N=5, K=1: one tile, one stage, one chunk.
@@ -122,7 +124,7 @@ def test_workspace_sizes(lib):
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, 7) == 0
     # cfp32_linear_geglu: M <= 8 holds partial sums for all 2F columns, even
     # for a single chunk; M > 8 the hi/lo planes.
-    assert cf.cfp32_linear_geglu_workspace_bytes(1, 7168, 4096) == 9 * 1 * 2 * 14336 * 4 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(1, 7168, 4096) == 8 * 1 * 2 * 14336 * 4 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 8) == 1 * 2 * 2 * 512 * 4 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 2 * 256 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 0) == 0

@@ -274,6 +274,18 @@ def main():
         b.synchronize()
         return a.elapsed_time(b) / n * 1e3
 
+    # The same decode projection recorded in a HIP graph (four calls, one per W
+    # copy) and replayed: what a captured decode loop pays per call.
+    gstream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gstream):
+        with torch.cuda.graph(graph, stream=gstream):
+            for j in range(4):
+                check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[j].data_ptr(), N_, y1.data_ptr(), N_, M_DEC, N_, K_,
+                                      dec_ws.data_ptr(), dec_ws_bytes, gstream.cuda_stream), "decode graph")
+    torch.cuda.synchronize()
+    gemv_graph_us = timed(lambda i: graph.replay(), 50) / 4
+    del graph
     # The decode projection with the weights as torch.nn.Linear stores them
     # ([N, K]): one dispatch, each output column streaming its own W row.
     Wts = [Ws[0].view(K_, N_).t().contiguous()]
@@ -372,6 +384,8 @@ def main():
             "gemv_1x4096x14336_us": round(gemv_us, 2),
             "gemv_GBps": round(dec_bytes / (gemv_us * 1e-6) / 1e9, 1),
             "gemv_frac_hbm": round(dec_bytes / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemv_graph_1x4096x14336_us": round(gemv_graph_us, 2),
+            "gemv_graph_frac_hbm": round(dec_bytes / (gemv_graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "gemv_nk_1x4096x14336_us": round(gemv_nk_us, 2),
             "gemv_nk_frac_hbm": round(dec_bytes / (gemv_nk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },

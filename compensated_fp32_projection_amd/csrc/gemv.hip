@@ -575,26 +575,30 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 // weights are one K-contiguous row) ----------------------------------------
 //
 // Every output column streams its own row of W, so no column strip problem
-// arises and no partial sums cross blocks: one dispatch.  A wave owns 16
-// columns over all of K; per 32-deep k-step, lane l loads 16 bytes of row
-// nb + l % 16 at k = 8 (l / 16) (exactly its MFMA B fragment, no LDS) and the
-// 8 matching values of x (two 16-byte loads), splits them and feeds one
-// v_mfma_f32_16x16x32_f16 with the hi and lo rows interleaved as above.
-// kNkU k-steps of loads are in flight per wave.  The K-reduction of each
-// output stays inside one MFMA chain, and the merge (and bias) happen in the
-// lane that holds both rows.  Needs K % 8 == 0 (a 16-byte granule is all in
-// or all out), W and x 16-byte aligned with ldw % 8 == 0 and ldx % 4 == 0.
-constexpr int kNkU = 4;  // measured: 4 k-steps in flight beat 8 and 16 (35 vs 54 and 46 us at 1x4096x14336)
+// arises and no partial sums cross blocks: one dispatch.  A block of 16 waves
+// owns 16 columns; per 32-deep k-step, lane l loads 16 bytes of row nb + l %
+// 16 at k = 8 (l / 16) (exactly its MFMA B fragment, no LDS) and the 8
+// matching values of x (two 16-byte loads), splits them and feeds one
+// v_mfma_f32_16x16x32_f16 with the hi and lo rows interleaved as above.  Wave
+// w takes k-steps w, w + 16, ..., so at any time the block's waves read one
+// contiguous 1 KiB run of each of its 16 rows; kNkU k-steps of loads are in
+// flight per wave.  The 16 waves' accumulators are summed in wave order
+// through LDS and the lane that holds both rows of an output merges it (and
+// adds the bias).  Needs K % 8 == 0 (a 16-byte granule is all in or all out),
+// W and x 16-byte aligned with ldw % 8 == 0 and ldx % 4 == 0.
+constexpr int kNkWaves = 16;
+constexpr int kNkU = 4;
 
-__global__ __launch_bounds__(256) void gemv_nk_kernel(const float *__restrict__ x, int64_t ldx,
-                                                      const uint16_t *__restrict__ w, int64_t ldw,
-                                                      float *__restrict__ y, int64_t ldy,
-                                                      const float *__restrict__ bias, int M, int64_t N, int64_t K)
+__global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__restrict__ x, int64_t ldx,
+                                                                const uint16_t *__restrict__ w, int64_t ldw,
+                                                                float *__restrict__ y, int64_t ldy,
+                                                                const float *__restrict__ bias, int M, int64_t N,
+                                                                int64_t K)
 {
+    __shared__ floatx4_t red[kNkWaves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nb = ((int64_t)blockIdx.x * 4 + wave) * 16;
-    if (nb >= N) return;  // wave-uniform
+    const int64_t nb = (int64_t)blockIdx.x * 16;
     const int64_t n = nb + (lane & 15);
     const int kq = lane >> 4;
     const int ai = lane & 15;
@@ -612,19 +616,19 @@ __global__ __launch_bounds__(256) void gemv_nk_kernel(const float *__restrict__ 
     const int x_kend = am < M ? (int)K - 8 * kq : INT_MIN;
 
     floatx4_t acc = floatx4_t{};
-    for (int k0 = 0; k0 < (int)K; k0 += 32 * kNkU) {
+    for (int k0 = 32 * wave; k0 < (int)K; k0 += 32 * kNkWaves * kNkU) {
         uint4 wv[kNkU];
         floatx4_t xa[kNkU], xb[kNkU];
 #pragma unroll
         for (int u = 0; u < kNkU; ++u) {
-            const int k = k0 + 32 * u;
+            const int k = k0 + 32 * kNkWaves * u;
             const int ox = k < x_kend ? x_base + 4 * k : kNoOffset;
             xa[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 0, 0));
             xb[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 16, 0));
         }
 #pragma unroll
         for (int u = 0; u < kNkU; ++u) {
-            const int k = k0 + 32 * u;
+            const int k = k0 + 32 * kNkWaves * u;
             const int ow = k < w_kend ? w_base + 2 * k : kNoOffset;
             wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, ow, 0, kStreamAux));
         }
@@ -640,14 +644,18 @@ __global__ __launch_bounds__(256) void gemv_nk_kernel(const float *__restrict__ 
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, wv[u]), acc, 0, 0, 0);
         }
     }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0 || n >= N) return;
+    floatx4_t t = red[0][lane];
+    for (int v = 1; v < kNkWaves; ++v) t += red[v][lane];
     // 16x16 accumulator: rows 4 kq + e, column lane % 16; rows 2m, 2m + 1 are
     // hi, lo of x row m.
-    if (n >= N) return;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int m = 2 * kq + q;
         if (m >= M) continue;
-        float v = merge_value(acc[2 * q], acc[2 * q + 1]);
+        float v = merge_value(t[2 * q], t[2 * q + 1]);
         if (bias) v = v + bias[n];
         y[m * ldy + n] = v;
     }
@@ -823,9 +831,10 @@ hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_
                       ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
                       N * ldw * 2 < kLimit && M * ldx * 4 < kLimit && K < kLimit / 64;
     if (fast) {
-        const int64_t blocks = (N + 63) / 64;
+        const int64_t blocks = (N + 15) / 16;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        gemv_nk_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias, (int)M, N, K);
+        gemv_nk_kernel<<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias, (int)M,
+                                                                            N, K);
         return hipGetLastError();
     }
     switch (M) {

@@ -8,15 +8,21 @@
 // for gfx950:
 //   * 512 threads (8 waves, 2 per SIMD), a 128 x 256 output tile (256 x 256
 //     with the hi and lo rows).  Each wave owns 64 rows x 64 columns of both
-//     products: 2 x 2 blocks of v_mfma_f32_32x32x16_f16 per product, 128
-//     FP32 accumulators per lane.  Every W fragment feeds a hi and a lo MFMA.
+//     products: 4 x 4 blocks of v_mfma_f32_16x16x32_f16 per product, 128
+//     FP32 accumulators per lane.  Every W fragment feeds four hi and four
+//     lo MFMAs.  The 16x16x32 form was measured against 32x32x16 blocks of
+//     the same wave tile (same LDS traffic, same results bit for bit): on
+//     normal-distributed data the chip runs at its power limit, and the
+//     16x16 form, with a quarter of the accumulator registers per
+//     instruction, draws less per product (8192 x 4096 x 14336: 1640 ->
+//     1530 us).
 //   * K in stages of 32.  Each stage (A_hi, A_lo: 128 x 32 FP16; W: 32 x 256
 //     FP16; 32 KiB) is fetched by 32 wave-wide 1 KiB LDS-DMA loads (4 per
 //     wave) that need no registers; three stages are in flight.
 //   * Waves 0-3 and waves 4-7 form two groups, one wave of each per SIMD.  A
 //     wave alternates a memory phase (issue its loads of stage s+3, read its
 //     fragments of stage s from LDS, wait for them) and a compute phase (the
-//     16 MFMAs of stage s at raised priority), with a block barrier after
+//     32 MFMAs of stage s at raised priority), with a block barrier after
 //     each.  The second group starts one barrier late, so while one group
 //     multiplies the other loads: each SIMD's matrix unit is fed by one wave
 //     while its partner waits on memory.
@@ -29,11 +35,14 @@
 //     DMA targets from the reads and inserts no waits of its own.
 //   * A sits in LDS as 16-byte k-granules, row-major, the granule order of
 //     each row XOR-ed with bits of the row index; an MFMA A fragment is one
-//     conflict-free ds_read_b128.  W sits N-contiguous (as in memory), the
-//     granule order of each k-row XOR-ed with the row's low bits; an MFMA B
-//     fragment (8 consecutive k of one column) is two ds_read_b64_tr_b16,
-//     the gfx950 LDS transpose read: in each 16-lane group, lane j's element
-//     e comes from element j%4 of the 8 bytes addressed by lane j/4 + 4e.
+//     conflict-free ds_read_b128 (lane l: row l % 16, k-granule l / 16).  W
+//     sits N-contiguous (as in memory), the granule order of each k-row
+//     XOR-ed with bits 0, 1 and 3 of k, so that the 8 k-rows one B read
+//     touches (k and k + 8 of 4 consecutive k) land in distinct banks; an
+//     MFMA B fragment (8 consecutive k of one column) is two
+//     ds_read_b64_tr_b16, the gfx950 LDS transpose read: in each 16-lane
+//     group, lane j's element e comes from element j%4 of the 8 bytes
+//     addressed by lane j/4 + 4e.
 //   * Loads outside the matrices get an offset no buffer reaches and read as
 //     zero, so partial tiles need no branches; stages past the end are loaded
 //     the same way, which keeps every wait count constant.
@@ -55,7 +64,7 @@ typedef short short8_t __attribute__((ext_vector_type(8)));
 constexpr int kT = 512;                             // 8 waves
 constexpr int BM = 128, BN = 256, BK = 32, NST = 4;
 constexpr int WTM = 64, WTN = 64;                   // wave tile (rows per product x columns)
-constexpr int TM = WTM / 32, TN = WTN / 32;         // 32x32 MFMA blocks per wave and product
+constexpr int TM = WTM / 16, TN = WTN / 16;         // 16x16 MFMA blocks per wave and product
 constexpr int WAVES_N = BN / WTN;                   // 4 waves across N, 2 across M
 constexpr int KG = BK / 8;                          // k-granules per A row per stage
 constexpr int A_SLOTS = BM * KG;                    // granules per A plane per stage (512)
@@ -101,9 +110,12 @@ __device__ __forceinline__ int a_slot(int plane, int row, int kg)
     return plane * A_SLOTS + row * KG + (kg ^ ((row >> 2) & 3));
 }
 
+// Granule swizzle of W k-row k: bits 0-1 of k select one of four 64-byte
+// quarters of a 256-byte bank window, bit 3 one of two 32-byte halves.
+__device__ __forceinline__ int w_swz(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
 __device__ __forceinline__ int w_slot(int k, int ng)
 {
-    return 2 * A_SLOTS + k * WG + (ng ^ ((k & 3) << 2));
+    return 2 * A_SLOTS + k * WG + (ng ^ w_swz(k));
 }
 
 // WNK variant (W given as [N, K], K-contiguous): W sits in LDS like A, as
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int wn = wave % WAVES_N;
 
     const int64_t nbm = (g.M + BM - 1) / BM;
-    static_assert(!GEGLU || (TN == 2 && !WNK && !SPLIT), "GEGLU: two 32-column blocks per wave, [K, N] W");
+    static_assert(!GEGLU || (TN == 4 && !WNK && !SPLIT), "GEGLU: four 16-column blocks per wave, [K, N] W");
     constexpr int TW = GEGLU ? BN / 2 : BN;  // output columns per block
     const int64_t ncols = GEGLU ? g.F : g.N;
     const int64_t nbn = (ncols + TW - 1) / TW;
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             w_kend[jj] = ok ? (int)(g.K - 8 * kg) : 0;  // K % 8 == 0: a granule is all in or all out
         } else {
             const int k = slot / WG;
-            const int ng = (slot % WG) ^ ((k & 3) << 2);
+            const int ng = (slot % WG) ^ w_swz(k);
             int64_t gcol;  // W column of this granule's first of 8 columns
             bool ok;
             if constexpr (GEGLU) {
@@ -278,42 +290,43 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         }
     };
 
-    floatx16_t acc_hi[TM][TN], acc_lo[TM][TN];
+    floatx4_t acc_hi[TM][TN], acc_lo[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc_hi[i][j] = floatx16_t{}, acc_lo[i][j] = floatx16_t{};
+        for (int j = 0; j < TN; ++j) acc_hi[i][j] = floatx4_t{}, acc_lo[i][j] = floatx4_t{};
 
     struct Frags {
         half8_t ah[TM], al[TM], bw[TN];
     };
-    // Per-lane parts of the fragment addresses.
-    const int a_row0 = wm * WTM + (lane & 31);
-    const int b_kl = 8 * (lane >> 5) + ((lane & 15) >> 2);                 // + 16 ks + 4 h
-    const int b_n0 = wn * WTN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // + 32 j
-    const int b_col0 = wn * WTN + (lane & 31);                             // WNK: + 32 j
+    // Per-lane parts of the fragment addresses (16x16x32 operand layout: lane
+    // l holds row / column l % 16 and k = 8 (l / 16) .. 8 (l / 16) + 7).
+    const int a_row0 = wm * WTM + (lane & 15);                       // + 16 i
+    const int a_kg = lane >> 4;
+    const int b_k0 = 8 * (lane >> 4) + ((lane & 15) >> 2);           // + 4 h
+    const int b_n0 = wn * WTN + 4 * (lane & 3);                      // + 16 j
+    const int b_col0 = wn * WTN + (lane & 15);                       // WNK: + 16 j
 
-    auto read_frags = [&](const uint4 *s, const uint4 *sa, int ks, Frags &f) {
-        const int kg = 2 * ks + (lane >> 5);
+    auto read_frags = [&](const uint4 *s, const uint4 *sa, Frags &f) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int row = a_row0 + 32 * i;
-            f.ah[i] = __builtin_bit_cast(half8_t, sa[a_slot(0, row, kg)]);
-            f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, kg)]);
+            const int row = a_row0 + 16 * i;
+            f.ah[i] = __builtin_bit_cast(half8_t, sa[a_slot(0, row, a_kg)]);
+            f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, a_kg)]);
         }
         if constexpr (WNK) {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot_nk(b_col0 + 32 * j, kg)]);
+                f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot_nk(b_col0 + 16 * j, a_kg)]);
             return;
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int n = b_n0 + 32 * j;
+            const int n = b_n0 + 16 * j;
             short4_t t[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int k = 16 * ks + 4 * h + b_kl;
+                const int k = b_k0 + 4 * h;
                 const int byte = w_slot(k, n >> 3) * 16 + (n & 7) * 2;
                 t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CFP32_LDS short4_t *)((CFP32_LDS char *)s + byte));
             }
@@ -323,12 +336,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     };
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                acc_hi[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
-                acc_lo[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
-            }
+            for (int j = 0; j < TN; ++j)
+                acc_hi[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
+        }
     };
 
     // SPLIT: lane's conversion unit: row 64*group + u/4, k-granule u%4.
@@ -351,20 +366,18 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     };
 
     const int64_t nk = (g.Ka + BK - 1) / BK;
-    Frags f0, f1;
+    Frags f0;
     // One stage for this wave: memory phase, barrier, compute phase, barrier.
     auto stage = [&](auto stage_tag, int64_t s) {
         constexpr int S = decltype(stage_tag)::value;
         issue(std::integral_constant<int, (S + 3) & 3>{}, (s + 3) * BK);
         const uint4 *buf = stage_buf<S>();
         const uint4 *abuf = SPLIT ? conv_buf<S & 1>() : buf;
-        read_frags(buf, abuf, 0, f0);
-        read_frags(buf, abuf, 1, f1);
+        read_frags(buf, abuf, f0);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
         block_barrier();
         __builtin_amdgcn_s_setprio(1);
         mfmas(f0);
-        mfmas(f1);
         if constexpr (SPLIT) {
             // Stage s + 1 landed (this group's loads) before the barrier above.
             convert(stage_buf<(S + 1) & 3>(), conv_buf<(S + 1) & 1>());
@@ -401,36 +414,39 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     if (group == 0) block_barrier();  // both groups pass the same number of barriers
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the trailing zero loads before the block exits
 
-    // Epilogue.  32x32 accumulator layout: lane holds column (lane & 31);
-    // element e holds row 8*(e/4) + 4*(lane/32) + (e%4) of the block.
+    // Epilogue.  16x16 accumulator layout: lane holds column (lane & 15);
+    // element e holds row 4*(lane/16) + e of the block.
     if constexpr (GEGLU) {
-        const int64_t col = n0 + 32 * wn + (lane & 31);
-        if (col >= g.F) return;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+        const int64_t col = n0 + 32 * wn + 16 * jj + (lane & 15);
+        if (col >= g.F) continue;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + e;
                 if (row >= g.M) continue;
-                float gate = merge_value(acc_hi[i][0][e], acc_lo[i][0][e]);
-                float up = merge_value(acc_hi[i][1][e], acc_lo[i][1][e]);
+                float gate = merge_value(acc_hi[i][jj][e], acc_lo[i][jj][e]);
+                float up = merge_value(acc_hi[i][jj + 2][e], acc_lo[i][jj + 2][e]);
                 if (g.bias) {
                     gate = gate + g.bias[col];
                     up = up + g.bias[g.F + col];
                 }
                 __builtin_nontemporal_store(gelu_value(gate) * up, g.y + row * g.ldy + col);
             }
+        }
         return;
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int64_t col = n0 + wn * WTN + j * 32 + (lane & 31);
+            const int64_t col = n0 + wn * WTN + j * 16 + (lane & 15);
             if (col >= g.N) continue;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            for (int e = 0; e < 4; ++e) {
+                const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + e;
                 if (row >= g.M) continue;
                 const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
                 // Outputs are written once: non-temporal stores keep them from

@@ -493,11 +493,14 @@ hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, 
                                     int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream)
 {
     GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr, 0};
+    // The 32 x 128 configuration: its running sums and accumulators fit two
+    // waves per SIMD (the 64 x 128 one needs more than 256 registers once the
+    // running sums are added and ran 12-45% slower; same bits).
     switch (k_steps_per_add) {
-    case 0: return launch_tile<TileMedium, 0>(g, stream);
-    case 1: return launch_tile<TileMedium, 1>(g, stream);
-    case 4: return launch_tile<TileMedium, 4>(g, stream);
-    case 16: return launch_tile<TileMedium, 16>(g, stream);
+    case 0: return launch_tile<TileSmall, 0>(g, stream);
+    case 1: return launch_tile<TileSmall, 1>(g, stream);
+    case 4: return launch_tile<TileSmall, 4>(g, stream);
+    case 16: return launch_tile<TileSmall, 16>(g, stream);
     default: return hipErrorInvalidValue;
     }
 }

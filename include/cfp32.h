@@ -119,7 +119,7 @@ CFP32_API cfp32_status cfp32_gemm(const uint16_t *a_hi, const uint16_t *a_lo, in
  *               (16: every MFMA starts from zero); 0 runs the same kernel
  *               configuration with plain accumulation, for comparison.  Any
  *               other value gives CFP32_ERR_INVALID_VALUE.
- * An accuracy mode: one 64 x 128 tile configuration, slower than cfp32_gemm
+ * An accuracy mode: one 32 x 128 tile configuration, slower than cfp32_gemm
  * (the cost is measured next to it).  Fixed order, repeatable bits.  One
  * kernel launch. */
 CFP32_API cfp32_status cfp32_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda,

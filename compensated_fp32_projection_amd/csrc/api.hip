@@ -161,7 +161,8 @@ size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K, int w_la
         return b == 0 ? 0 : b + kAlign;
     }
     if (!extent_ok(M, split_ld(K))) return 0;
-    return 2 * plane_bytes(M, K) + kAlign;
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
+    return 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0) + kAlign;
 }
 
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -220,6 +221,15 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
     // read whole 16-byte groups past K.
     hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, ldh, s);
     if (e != hipSuccess) return hip_fail(e);
+    // Grids too small for the GPU: K split into chunks (partial sums after the
+    // planes in the workspace) and a merge dispatch.
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
+    if (sp.chunks > 1) {
+        float *part = reinterpret_cast<float *>(base + 2 * plane_bytes(M, K));
+        e = cfp32::launch_gemm_chunked(hi, lo, ldh, w, ldw, y, ldy, M, N, K, /*a_zero_padded=*/true, s, bias, nk,
+                                       part, sp.workspace_bytes);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K,
                                        /*a_zero_padded=*/true, s, bias, nk));
 }

@@ -81,6 +81,14 @@ struct GemmArgs {
     int64_t M, N, K;
     const float *bias;  // FP32 [N] added to y after the merge, or null
     int geglu_rmw;      // y holds a GEGLU gate on entry: y = gelu(y) * (merged value + bias)
+    // Split K: K is cut into 64-deep units (one stage each), dealt in order to
+    // `kchunks` chunks as evenly as possible, the cuts the LDS-DMA kernel
+    // makes; block b computes tile b % tiles over chunk b / tiles and writes
+    // its unmerged C_hi, C_lo to part[chunk][row][2][n_pad].  kchunks == 1:
+    // no split (the only case with SEP > 0 or geglu_rmw).
+    int64_t kchunks;
+    float *part;
+    int64_t n_pad;
 };
 
 // Slot of A granule (k-group kg, tile row `row`) of plane p inside a stage.
@@ -133,7 +141,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     const int64_t nbm = (g.M + T::BM - 1) / T::BM;
     const int64_t nbn = (g.N + T::BN - 1) / T::BN;
     const int64_t total = nbm * nbn;
-    int64_t bid = blockIdx.x;
+    const int64_t chunk = (int64_t)blockIdx.x / total;  // 0 unless K is split
+    int64_t bid = (int64_t)blockIdx.x % total;
     {
         const int64_t q = total / kXcds, r = total % kXcds;
         const int64_t xcd = bid % kXcds, local = bid / kXcds;
@@ -146,6 +155,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     const int64_t tile_n = (bid % group_span) / gsize;
     const int64_t m0 = tile_m * T::BM;
     const int64_t n0 = tile_n * T::BN;
+
+    // This block's 64-deep K stages [u_begin, u_end) and the first k its loads
+    // may not reach.
+    const int64_t units = (g.K + kBK - 1) / kBK;
+    const int64_t u_base = units / g.kchunks, u_extra = units % g.kchunks;
+    const int64_t u_begin = chunk * u_base + (chunk < u_extra ? chunk : u_extra);
+    const int64_t u_end = u_begin + u_base + (chunk < u_extra ? 1 : 0);
+    const int64_t k_begin = kBK * u_begin;
+    const int64_t klim = kBK * u_end < g.K ? kBK * u_end : g.K;
 
     floatx16_t acc_hi[T::TM][T::TN];
     floatx16_t acc_lo[T::TM][T::TN];
@@ -248,8 +266,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             const int kg = c & 7, row = c >> 3;
             const int64_t gm = m0 + row, gk = k0 + 8 * kg;
             if (gm < g.M) {
-                ra[0][i] = load_row8<AL_A>(g.a_hi + gm * g.lda, gk, g.K);
-                ra[1][i] = load_row8<AL_A>(g.a_lo + gm * g.lda, gk, g.K);
+                ra[0][i] = load_row8<AL_A>(g.a_hi + gm * g.lda, gk, klim);
+                ra[1][i] = load_row8<AL_A>(g.a_lo + gm * g.lda, gk, klim);
             } else {
                 ra[0][i] = make_uint4(0, 0, 0, 0);
                 ra[1][i] = make_uint4(0, 0, 0, 0);
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
                 const int c = tid + kThreads * q;
                 const int64_t gn = n0 + (c >> 3), gk = k0 + 8 * (c & 7);
-                rw[q >> 3][q & 7] = gn < g.N ? load_row8<AL_W>(g.w + gn * g.ldw, gk, g.K) : make_uint4(0, 0, 0, 0);
+                rw[q >> 3][q & 7] = gn < g.N ? load_row8<AL_W>(g.w + gn * g.ldw, gk, klim) : make_uint4(0, 0, 0, 0);
             }
             return;
         }
@@ -273,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
                     const int64_t gk = k0 + 8 * kgw + r;
-                    rw[j][r] = gk < g.K ? load_row8<AL_W>(g.w + gk * g.ldw, gn, g.N) : make_uint4(0, 0, 0, 0);
+                    rw[j][r] = gk < klim ? load_row8<AL_W>(g.w + gk * g.ldw, gn, g.N) : make_uint4(0, 0, 0, 0);
                 }
             }
         }
@@ -370,26 +388,28 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     // is fetched into registers; one barrier per stage.  Full stages use the
     // buffer loads, so the main loop has no branch; the ragged last stage (if
     // K is not a multiple of 64) is peeled off and uses guarded loads.
-    const int64_t nk = (g.K + kBK - 1) / kBK;
-    const int64_t nk_full = BUF ? g.K / kBK : 0;
+    // (Chunk boundaries are multiples of 64, so only the chunk that ends at K
+    // can have a ragged last stage.)
+    const int64_t nk = u_end - u_begin;
+    const int64_t nk_full = BUF ? (klim - k_begin) / kBK : 0;
     if (nk == 0) {
         // K == 0: nothing to accumulate; the epilogue writes +0.
     } else {
         if (nk_full > 0)
-            load_stage_buf(0);
+            load_stage_buf(k_begin);
         else
-            load_stage(0);
+            load_stage(k_begin);
         store_stage(0);
         __syncthreads();
         int64_t kt = 0;
         for (; kt + 1 < nk_full; ++kt) {
-            load_stage_buf((kt + 1) * kBK);
+            load_stage_buf(k_begin + (kt + 1) * kBK);
             compute_stage((int)(kt & 1), kt);
             store_stage((int)((kt + 1) & 1));
             __syncthreads();
         }
         for (; kt + 1 < nk; ++kt) {
-            load_stage((kt + 1) * kBK);
+            load_stage(k_begin + (kt + 1) * kBK);
             compute_stage((int)(kt & 1), kt);
             store_stage((int)((kt + 1) & 1));
             __syncthreads();
@@ -413,6 +433,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
                 if (row >= g.M) continue;
                 const float h = SEP ? sum_hi[i][j][e] : acc_hi[i][j][e];
                 const float l = SEP ? sum_lo[i][j][e] : acc_lo[i][j][e];
+                if (g.kchunks > 1) {
+                    float *p = g.part + ((chunk * g.M + row) * 2) * g.n_pad + col;
+                    p[0] = h;
+                    p[g.n_pad] = l;
+                    continue;
+                }
                 if (g.y) {
                     float v = merge_value(h, l);
                     if (g.bias) v = v + g.bias[col];
@@ -432,7 +458,7 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 template <class T, int SEP = 0, bool WNK = false>
 hipError_t launch_tile(const GemmArgs &g, hipStream_t stream)
 {
-    const int64_t blocks = ((g.M + T::BM - 1) / T::BM) * ((g.N + T::BN - 1) / T::BN);
+    const int64_t blocks = ((g.M + T::BM - 1) / T::BM) * ((g.N + T::BN - 1) / T::BN) * g.kchunks;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const bool al_a = (g.lda % 8 == 0) && aligned16(g.a_hi) && aligned16(g.a_lo);
     const bool al_w = (g.ldw % 8 == 0) && aligned16(g.w);
@@ -464,16 +490,19 @@ int64_t tiles_of(int64_t M, int64_t N)
 
 }  // namespace
 
-// Tile choice: the largest tile that still gives at least one block per CU
-// (256 CUs); below that, the smallest tile, which has the most blocks.
+// Tile choice: the LDS-DMA kernel (128 x 256 tiles) from three quarters of
+// a block per CU (192 tiles) up, the generic kernel in its largest tile that
+// still gives one block per CU below that, else its smallest tile.  (At M =
+// 512, K = 4096, N = 14336, 224 tiles, the whole projection took 123 us with
+// the LDS-DMA kernel and 174 us with the generic 64 x 128 one.)
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
                        const float *bias, bool w_nk, bool geglu_rmw)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias, geglu_rmw ? 1 : 0};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias, geglu_rmw ? 1 : 0, 1, nullptr, 0};
     constexpr int64_t kCus = 256;
-    if (tiles_of<TileLarge>(M, N) >= kCus && !geglu_rmw) {
+    if (tiles_of<TileLarge>(M, N) >= kCus * 3 / 4 && !geglu_rmw) {
         const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
                                              a_zero_padded, stream, bias, w_nk);
         if (e != hipErrorNotSupported) return e;
@@ -484,15 +513,63 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
     return w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
 }
 
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
+{
+    GemmSplitPlan p{1, 0, 0};
+    // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
+    // 35-52 us; at M = 128 and 256 it measured no better than the generic
+    // kernel (75 vs 78 us, 122 vs 98 us), the partial sums costing what the
+    // wider grid gains.
+    constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kMaxRows = 64;
+    if (M <= kGemvMaxRows || M > kMaxRows || N <= 0 || K <= 0 || K % 8) return p;
+    if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
+    const int64_t tiles = ((M + kTileRows - 1) / kTileRows) * ((N + kTileCols - 1) / kTileCols);
+    if (tiles >= 128) return p;
+    int64_t c = 256 / tiles;
+    for (int64_t cc = c; cc >= 1 && cc > c - 8; --cc)
+        if ((cc * tiles) % 8 == 0) {
+            c = cc;
+            break;
+        }
+    const int64_t units = (K + kUnit - 1) / kUnit;
+    if (c > units / kMinUnits) c = units / kMinUnits;
+    // The partial sums (8 M N bytes per chunk, written and read back) stay
+    // within a quarter of W's 2 K N bytes.
+    if (c > K / (16 * M)) c = K / (16 * M);
+    if (c < 2) return p;
+    p.chunks = c;
+    p.n_pad = (N + 63) / 64 * 64;
+    p.workspace_bytes = (size_t)c * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                               int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                               bool a_zero_padded, hipStream_t stream, const float *bias, bool w_nk, float *part,
+                               size_t part_bytes)
+{
+    const GemmSplitPlan p = gemm_split_plan(M, N, K);
+    if (p.chunks < 2 || !part || part_bytes < p.workspace_bytes) return hipErrorNotSupported;
+    hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, nullptr, 0, nullptr, nullptr, 0, M, N, K, a_zero_padded,
+                                   stream, nullptr, w_nk, p.chunks, part, p.n_pad);
+    if (e == hipErrorNotSupported) {
+        GemmArgs g{a_hi, a_lo, lda, w, ldw, nullptr, 0, nullptr, nullptr, 0, M, N, K, nullptr, 0, p.chunks, part,
+                   p.n_pad};
+        e = w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
+    }
+    if (e != hipSuccess) return e;
+    return launch_partial_merge(part, p.n_pad, p.chunks, M, N, y, ldy, bias, stream);
+}
+
 // Separate-addition accumulation (see gemm_kernel): one tile configuration,
-// 64 x 128 (a wave holds 64 running sums next to its 64 accumulators).
+// 32 x 128 (a wave holds 32 running sums next to its 32 accumulators).
 // k_steps_per_add: 0 (plain accumulation in the same configuration, for
 // comparison), 1, 4 or 16 sixteen-deep k-steps per separate addition.
 hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                                     int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                                     int64_t M, int64_t N, int64_t K, int k_steps_per_add, hipStream_t stream)
 {
-    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr, 0};
+    GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, nullptr, 0, 1, nullptr, 0};
     // The 32 x 128 configuration: its running sums and accumulators fit two
     // waves per SIMD (the 64 x 128 one needs more than 256 registers once the
     // running sums are added and ran 12-45% slower; same bits).

@@ -150,6 +150,15 @@ struct DmaArgs {
     int64_t Ka;  // columns of A that may be read: K, or K rounded up to 8 when A is zero-padded
     const float *bias;  // FP32 [N] added to y after the merge, or null
     int64_t F;          // GEGLU variant: output columns; W, bias are [.., 2F] (gate | up)
+    // Split K (plain variants): K is cut into 64-deep units, dealt in order to
+    // `kchunks` chunks as evenly as possible (the generic kernel cuts at the
+    // same places, so both give the same partial sums); block b computes tile
+    // b % tiles over chunk b / tiles and writes its unmerged C_hi, C_lo to
+    // part[chunk][row][2][n_pad] (C_hi, then C_lo at + n_pad); a merge
+    // dispatch sums the chunks in order.  kchunks == 1: no split, no part.
+    int64_t kchunks;
+    float *part;
+    int64_t n_pad;
 };
 
 // FP32 A in LDS (SPLIT variant): each 128-byte row of 32 floats is 8
@@ -193,7 +202,20 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     const int64_t ncols = GEGLU ? g.F : g.N;
     const int64_t nbn = (ncols + TW - 1) / TW;
     int64_t tile_m, tile_n;
-    tile_of_block(blockIdx.x, nbm, nbn, tile_m, tile_n);
+    const int64_t tiles = nbm * nbn;
+    const int64_t chunk = (int64_t)blockIdx.x / tiles;  // 0 unless K is split
+    tile_of_block((int64_t)blockIdx.x % tiles, nbm, nbn, tile_m, tile_n);
+    // This block's K stages and the first k its loads may not reach.
+    const int64_t nk_all = (g.Ka + BK - 1) / BK;
+    const int64_t units = (g.Ka + 63) / 64;
+    const int64_t u_base = units / g.kchunks, u_extra = units % g.kchunks;
+    const int64_t u_begin = chunk * u_base + (chunk < u_extra ? chunk : u_extra);
+    const int64_t u_end = u_begin + u_base + (chunk < u_extra ? 1 : 0);
+    const int64_t s_begin = 2 * u_begin;
+    const int64_t nk = (2 * u_end < nk_all ? 2 * u_end : nk_all) - s_begin;
+    const int64_t k_end = 64 * u_end;
+    const int64_t ka_stop = k_end < g.Ka ? k_end : g.Ka;  // A (zero-padded to Ka)
+    const int64_t kw_stop = k_end < g.K ? k_end : g.K;    // W, and A in the SPLIT variant
     const int64_t m0 = tile_m * BM;
     const int64_t n0 = tile_n * TW;
 
@@ -224,7 +246,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             const int gr = (slot % 8) ^ (row & 7);
             const bool ok = m0 + row < g.M;
             a_off[jj] = ok ? (int)(((m0 + row) * g.lda + 4 * gr) * 4) : kNoOffset;
-            a_kend[jj] = ok ? (int)(g.K - 4 * gr) : 0;  // K % 4 == 0: a granule is all in or all out
+            a_kend[jj] = ok ? (int)(kw_stop - 4 * gr) : 0;  // K % 4 == 0: a granule is all in or all out
         }
     } else {
         const int slot = 64 * wave + lane;
@@ -232,7 +254,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         const int kg = (slot % KG) ^ ((row >> 2) & 3);
         const bool ok = m0 + row < g.M;
         a_off[0] = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
-        a_kend[0] = ok ? (int)(g.Ka - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
+        a_kend[0] = ok ? (int)(ka_stop - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
         a_off[1] = a_off[0];
         a_kend[1] = a_kend[0];
     }
@@ -244,7 +266,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             const int kg = (slot % KG) ^ ((n >> 2) & 3);
             const bool ok = n0 + n < g.N;
             w_off[jj] = ok ? (int)(((n0 + n) * g.ldw + 8 * kg) * 2) : kNoOffset;
-            w_kend[jj] = ok ? (int)(g.K - 8 * kg) : 0;  // K % 8 == 0: a granule is all in or all out
+            w_kend[jj] = ok ? (int)(kw_stop - 8 * kg) : 0;  // K % 8 == 0: a granule is all in or all out
         } else {
             const int k = slot / WG;
             const int ng = (slot % WG) ^ w_swz(k);
@@ -260,7 +282,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
                 ok = gcol < g.N;
             }
             w_off[jj] = ok ? (int)((k * g.ldw + gcol) * 2) : kNoOffset;
-            w_kend[jj] = ok ? (int)(g.K - k) : 0;
+            w_kend[jj] = ok ? (int)(kw_stop - k) : 0;
         }
     }
 
@@ -365,7 +387,6 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         dst[a_slot(1, row, kg)] = __builtin_bit_cast(uint4, l);
     };
 
-    const int64_t nk = (g.Ka + BK - 1) / BK;
     Frags f0;
     // One stage for this wave: memory phase, barrier, compute phase, barrier.
     auto stage = [&](auto stage_tag, int64_t s) {
@@ -389,9 +410,9 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         block_barrier();
     };
 
-    issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, BK);
-    issue(std::integral_constant<int, 2>{}, 2 * BK);
+    issue(std::integral_constant<int, 0>{}, s_begin * BK);
+    issue(std::integral_constant<int, 1>{}, (s_begin + 1) * BK);
+    issue(std::integral_constant<int, 2>{}, (s_begin + 2) * BK);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS_PER_WAVE));  // stage 0 landed for this wave
     block_barrier();
     if constexpr (SPLIT) {
@@ -403,14 +424,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     if (group == 1) block_barrier();  // the second group runs one phase behind
     const int64_t nk4 = nk / NST * NST;
     for (int64_t s0 = 0; s0 < nk4; s0 += NST) {
-        stage(std::integral_constant<int, 0>{}, s0);
-        stage(std::integral_constant<int, 1>{}, s0 + 1);
-        stage(std::integral_constant<int, 2>{}, s0 + 2);
-        stage(std::integral_constant<int, 3>{}, s0 + 3);
+        stage(std::integral_constant<int, 0>{}, s_begin + s0);
+        stage(std::integral_constant<int, 1>{}, s_begin + s0 + 1);
+        stage(std::integral_constant<int, 2>{}, s_begin + s0 + 2);
+        stage(std::integral_constant<int, 3>{}, s_begin + s0 + 3);
     }
-    if (nk4 < nk) stage(std::integral_constant<int, 0>{}, nk4);
-    if (nk4 + 1 < nk) stage(std::integral_constant<int, 1>{}, nk4 + 1);
-    if (nk4 + 2 < nk) stage(std::integral_constant<int, 2>{}, nk4 + 2);
+    if (nk4 < nk) stage(std::integral_constant<int, 0>{}, s_begin + nk4);
+    if (nk4 + 1 < nk) stage(std::integral_constant<int, 1>{}, s_begin + nk4 + 1);
+    if (nk4 + 2 < nk) stage(std::integral_constant<int, 2>{}, s_begin + nk4 + 2);
     if (group == 0) block_barrier();  // both groups pass the same number of barriers
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the trailing zero loads before the block exits
 
@@ -451,6 +472,12 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
                 const float h = acc_hi[i][j][e], l = acc_lo[i][j][e];
                 // Outputs are written once: non-temporal stores keep them from
                 // evicting the A and W panels other tiles still read from L2.
+                if (g.kchunks > 1) {
+                    float *p = g.part + ((chunk * g.M + row) * 2) * g.n_pad + col;
+                    __builtin_nontemporal_store(h, p);
+                    __builtin_nontemporal_store(l, p + g.n_pad);
+                    continue;
+                }
                 if (g.y) {
                     float v = merge_value(h, l);
                     if (g.bias) v = v + g.bias[col];
@@ -482,8 +509,9 @@ inline bool w_fits(int64_t ldw, int64_t N, int64_t K, bool w_nk)
 hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                            int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
-                           const float *bias, bool w_nk)
+                           const float *bias, bool w_nk, int64_t kchunks, float *part, int64_t n_pad)
 {
+    if (kchunks < 1 || (kchunks > 1 && (!part || n_pad < N))) return hipErrorNotSupported;
     if (K <= 0 || lda % 8 || ldw % 8 || !aligned16(a_hi) || !aligned16(a_lo) || !aligned16(w))
         return hipErrorNotSupported;
     if (w_nk && K % 8) return hipErrorNotSupported;
@@ -492,9 +520,9 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
     // Every byte offset a lane forms (including a tile's overhang) stays below kNoOffset.
     constexpr int64_t kLim = kNoOffset - (1 << 20);
     if ((M + BM) * lda * 2 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
-    const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN) * kchunks;
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias, 0};
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias, 0, kchunks, part, n_pad};
     if (w_nk)
         gemm_dma_kernel<false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
@@ -517,7 +545,7 @@ hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w,
     if ((M + BM) * lda * 4 >= kLim || !w_fits(ldw, N, K, w_nk)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K, bias, 0};
+    DmaArgs g{nullptr, nullptr, a, lda, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K, K, bias, 0, 1, nullptr, 0};
     if (w_nk)
         gemm_dma_kernel<true, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
@@ -540,7 +568,7 @@ hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int
     if ((M + BM) * lda * 2 >= kLim || !w_fits(ldw, 2 * F, K, false)) return hipErrorNotSupported;
     const int64_t blocks = ((M + BM - 1) / BM) * ((F + BN / 2 - 1) / (BN / 2));
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
-    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, out, ldo, nullptr, nullptr, ldo, M, 2 * F, K, Ka, bias, F};
+    DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, out, ldo, nullptr, nullptr, ldo, M, 2 * F, K, Ka, bias, F, 1, nullptr, 0};
     gemm_dma_kernel<false, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();
 }

@@ -742,6 +742,16 @@ hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_
 
 // About one block per CU over all column tiles; a chunk has at least one
 // stage of 32 rows.
+hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t N, float *y,
+                                int64_t ldy, const float *bias, hipStream_t stream)
+{
+    const int64_t outs = M * N;
+    if (M > 0x7FFFFFFF || (outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y,
+                                                                                 ldy, bias);
+    return hipGetLastError();
+}
+
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
 {
     GemvPlan p{};

@@ -37,10 +37,46 @@ hipError_t launch_gemm_separate_add(const uint16_t *a_hi, const uint16_t *a_lo, 
 
 // LDS-DMA variant for aligned operands (gemm_dma.hip); hipErrorNotSupported
 // when the operands do not allow it, in which case nothing was enqueued.
+// kchunks > 1: split K as GemmSplitPlan describes and write the unmerged
+// per-chunk products to `part` ([kchunks][M][2][n_pad]) instead of y, c_hi,
+// c_lo (launch_gemm_chunked adds the merge).
 hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                            int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                            int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
-                           const float *bias = nullptr, bool w_nk = false);
+                           const float *bias = nullptr, bool w_nk = false, int64_t kchunks = 1,
+                           float *part = nullptr, int64_t n_pad = 0);
+
+// Split K for 8 < M <= 64 on grids too small for the GPU (fewer than 128
+// output tiles of 128 x 256): K is cut into 64-deep units, dealt in order to
+// `chunks` chunks as evenly as possible (at least 4 units each; chunks x
+// tiles about 256, a multiple of 8 where one is within reach; partial sums
+// at most a quarter of W's bytes); each chunk's C_hi, C_lo go to FP32
+// partial sums ([chunks][M][2][n_pad], workspace_bytes in all) that a merge
+// dispatch adds in chunk order, then merges.  chunks == 1 (and no
+// workspace) otherwise, or when K % 8 != 0 or K is short.  Depends on M, N,
+// K only, so every kernel that takes the plan cuts at the same places and
+// gives the same bits.
+struct GemmSplitPlan {
+    int64_t chunks;
+    int64_t n_pad;
+    size_t workspace_bytes;
+};
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
+
+// The split-K GEMM of the plan plus the merge dispatch (y = merge of the
+// chunk sums, + bias).  hipErrorNotSupported, with nothing enqueued, when the
+// plan has one chunk or `part` is missing or smaller than the plan's
+// workspace.  The LDS-DMA kernel when the operands allow it, else the
+// generic kernel (same cuts, same bits).
+hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
+                               int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                               bool a_zero_padded, hipStream_t stream, const float *bias, bool w_nk, float *part,
+                               size_t part_bytes);
+
+// Sum of `chunks` partial sums part[c][m][2][n_pad] in chunk order, merged
+// into y [M, N] (+ bias) (gemv.hip's merge dispatch).
+hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t N, float *y,
+                                int64_t ldy, const float *bias, hipStream_t stream);
 
 // LDS-DMA GEMM on FP32 A, split in registers (one launch for the whole
 // projection); hipErrorNotSupported, with nothing enqueued, unless K % 4 == 0,

@@ -134,6 +134,23 @@ def test_workspace_sizes(lib):
     # two FP16 planes of M x roundup(K, 8), 256-byte aligned, plus alignment slack
     assert cf.cfp32_linear_workspace_bytes(9, 5, 1) == 2 * 256 + 256
     assert cf.cfp32_linear_workspace_bytes(4096, 4096, 4096) == 2 * 4096 * 4096 * 2 + 256
+    # M > 8 with fewer than 128 output tiles of 128 x 256 and K % 8 == 0: K is
+    # split (chunks x tiles about 256, a multiple of 8 where within reach, at
+    # least four 64-deep units per chunk) and FP32 partial sums
+    # [chunks][M][2][N rounded up to 64] follow the planes.  M=64, N=14336
+    # (56 tiles), K=4096 (64 units): 256 // 56 = 4 chunks, 224 blocks.
+    planes = 2 * 64 * 4096 * 2
+    assert cf.cfp32_linear_workspace_bytes(64, 14336, 4096) == planes + 4 * 64 * 2 * 14336 * 4 + 256
+    # M=40, N=520 (3 tiles), K=4104 (65 units): 85 chunks wanted, 80 for a
+    # multiple of 8 blocks, 65 // 4 = 16 by length, 4104 // (16 * 40) = 6 by
+    # the partial-sum bytes: 6 chunks, N rounded up to 576.
+    planes = 2 * ((40 * 4104 * 2 + 255) // 256 * 256)
+    assert cf.cfp32_linear_workspace_bytes(40, 520, 4104) == planes + 6 * 40 * 2 * 576 * 4 + 256
+    # M > 64, K % 8 != 0, K too short for two chunks, or enough tiles: planes only.
+    assert cf.cfp32_linear_workspace_bytes(300, 777, 1000) == 2 * ((300 * 1000 * 2 + 255) // 256 * 256) + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 14336, 4100) == 2 * ((64 * 4104 * 2 + 255) // 256 * 256) + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 14336, 256) == 2 * 64 * 256 * 2 + 256
+    assert cf.cfp32_linear_workspace_bytes(512, 14336, 4096) == 2 * 512 * 4096 * 2 + 256
 
 
 def test_empty_problems_are_no_ops(lib):

@@ -1,0 +1,92 @@
+"""GPU tests of the split-K path of cfp32_linear / cfp32_linear_ex: 8 < M <=
+64 with fewer than 128 output tiles of 128 x 256 and K % 8 == 0 (batched
+decode shapes).  K is cut into chunks of 64-deep units, each chunk's C_hi, C_lo go
+to FP32 partial sums, and a merge dispatch adds them in chunk order and
+merges once.  The plan depends on M, N, K only, so:
+  * y is within 1e-5 * sum|a w| of the FP64 reference and finite;
+  * y's error is at least 16x below that of the single-FP16 product;
+  * repeated calls give identical bits;
+  * the LDS-DMA kernel (aligned W) and the generic kernel (unaligned W) give
+    identical bits, and so do [K, N] and [N, K] weights;
+  * the bias is one more FP32 addition after the merge.
+"""
+import numpy as np
+import pytest
+import torch
+
+import compensated_fp32_projection_amd as cf
+import oracle
+from compensated_fp32_projection_amd import workloads
+from gpu_helpers import assert_better_than_single, assert_within_tolerance, note, stream_handle, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run(A, W, layout=cf.W_KN, w_offset=0, bias=None):
+    M, K = A.shape
+    N = W.shape[1]
+    Wl = W if layout == cf.W_KN else np.ascontiguousarray(W.T)
+    rows, cols = Wl.shape
+    ldw = cols + w_offset
+    wb = np.zeros(rows * ldw + w_offset, np.uint16)
+    wb[w_offset:].reshape(rows, ldw)[:, :cols] = Wl.view(np.uint16)
+    dx, dw = to_dev(A), to_dev(wb)
+    db = to_dev(bias) if bias is not None else None
+    y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, layout)
+    ws = torch.full((max(need, 1),), 0xFF, dtype=torch.uint8, device="cuda")  # contents must not matter
+    st = cf.cfp32_linear_ex(dx.data_ptr(), K, dw.data_ptr() + 2 * w_offset, ldw, layout,
+                            db.data_ptr() if db is not None else None, y.data_ptr(), N, M, N, K,
+                            ws.data_ptr() if need else None, need, stream_handle())
+    assert st == cf.OK, cf.cfp32_status_string(st)
+    return to_host(y)
+
+
+def planes_bytes(M, K):
+    ld = (K + 7) // 8 * 8
+    return 2 * ((M * ld * 2 + 255) // 256 * 256)
+
+
+# (M, K, N): the smallest M of the GEMM path, ragged N and K; many chunks;
+# the batched-decode FFN shape at the largest M that splits; a ragged last
+# unit of K; a chunk count that is not a power of two.
+SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), (24, 2000, 777)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_split_k_against_reference(M, K, N):
+    need = cf.cfp32_linear_workspace_bytes(M, N, K)
+    assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
+    A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
+    note(f"split-K {M}x{K}x{N}")
+    y = run(A, W)
+    rows = np.arange(M)
+    y64, abs64 = oracle.y64(A[rows], W)
+    assert_within_tolerance(y[rows], y64, abs64, f"split-K {M}x{K}x{N}")
+    _, ch, _ = oracle.linear_cf32(A[rows[:16]], W)
+    assert_better_than_single(y[rows[:16]], ch, y64[:16], abs64[:16], f"split-K {M}x{K}x{N}")
+    y2 = run(A, W)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+
+
+@pytest.mark.parametrize("M,K,N", [(9, 1000, 777), (40, 4104, 520), (24, 2000, 777)])
+def test_split_k_kernels_and_layouts_agree(M, K, N):
+    """Aligned [K, N] (LDS-DMA kernel), unaligned [K, N] (generic kernel) and
+    [N, K] weights: the same cuts, so the same bits."""
+    A, W = workloads.random_case(M + 3 * K + N, M, K, N, a_scale=20.0)
+    note(f"split-K kernels agree {M}x{K}x{N}")
+    y_dma = run(A, W)
+    y_gen = run(A, W, w_offset=1)
+    y_nk = run(A, W, layout=cf.W_NK)
+    assert np.array_equal(y_dma.view(np.uint32), y_gen.view(np.uint32))
+    assert np.array_equal(y_dma.view(np.uint32), y_nk.view(np.uint32))
+
+
+def test_split_k_bias_is_one_addition():
+    M, K, N = 32, 2048, 1000
+    A, W = workloads.random_case(99, M, K, N, a_scale=20.0)
+    bias = (np.random.default_rng(5).standard_normal(N) * 3).astype(np.float32)
+    note("split-K bias")
+    y0 = run(A, W)
+    y1 = run(A, W, bias=bias)
+    assert np.array_equal(y1.view(np.uint32), (y0 + bias[None, :]).astype(np.float32).view(np.uint32))

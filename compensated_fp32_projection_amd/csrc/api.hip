@@ -162,7 +162,13 @@ size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K, int w_la
     }
     if (!extent_ok(M, split_ld(K))) return 0;
     const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
-    return 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0) + kAlign;
+    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
+    // [K, N] with 8 < M <= 16 takes the small-M dispatches when W allows
+    // 16-byte loads, else the GEMM path: room for either.
+    const size_t small_m = (w_layout == CFP32_W_KN && M <= cfp32::kGemvMaxRowsKN)
+                               ? cfp32::gemv_plan(M, N, K).workspace_bytes
+                               : 0;
+    return (gemm_path > small_m ? gemm_path : small_m) + kAlign;
 }
 
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -199,6 +205,15 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
                                            bias));
     }
 
+    if (!nk && M <= cfp32::kGemvMaxRowsKN && K > 0) {
+        // Up to 16 rows of x: the small-M product and merge dispatches (each W
+        // fragment serves two groups of 8 rows, W streams once); they
+        // enqueue nothing and return hipErrorNotSupported when W does not
+        // allow 16-byte loads, and the GEMM path below runs instead.
+        const hipError_t e = cfp32::launch_gemv(x, ldx, w, ldw, y, ldy, M, N, K, reinterpret_cast<float *>(base),
+                                                need - kAlign, s, bias);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     if (K == 0)  // nothing to split: the product of an empty sum is +0
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s, bias));

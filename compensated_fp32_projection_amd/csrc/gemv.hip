@@ -56,8 +56,11 @@ constexpr int kT = 256;                   // 4 waves, 128 columns each
 constexpr int kBK = 32;                   // rows of W per stage (the MFMA's k)
 constexpr int kRowSlots = kTileN / 8;     // 16-byte granules per W row in LDS
 constexpr int kWSlots = kBK * kRowSlots;  // 2048 granules: 32 KiB of W per stage
-constexpr int kXSlots = 64;               // 1 KiB: x[8 rows][32 columns] FP32 per stage
-constexpr int kLoadsPerStage = kBK / (kT / 64) + 1;  // per wave: 8 W rows + 1 x load
+constexpr int kMaxGroups = 2;             // matrix-unit kernel: up to 2 groups of 8 rows of x
+constexpr int kXSlots = 64 * kMaxGroups;  // x[8 G rows][32 columns] FP32 per stage (G KiB)
+// Loads per wave per stage: 8 W rows + one x load per group of 8 rows.
+template <int G>
+constexpr int loads_per_stage() { return kBK / (kT / 64) + G; }
 
 // Separate LDS objects per ring buffer (and for W and x), so that the
 // compiler can tell which DMA fills which buffer and adds no waits of its own.
@@ -121,8 +124,10 @@ struct GemvArgs {
     int geglu;          // partial sums always (a GEGLU merge follows), never y
 };
 
+template <int G>
 __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
 {
+    constexpr int kLoadsPerStage = loads_per_stage<G>();
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Chunk c holds `base` stages, plus one for the first `extra` chunks.
@@ -144,8 +149,9 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(g.x), 0, (int)(g.M * g.ldx * 4), kBufferWord3);
 
     // DMA sources of this lane.  W: the wave loads rows 8 wave + j of a stage,
-    // lane l the granule that belongs at position l of that row.  x: the wave
-    // loads rows 2 wave and 2 wave + 1, lane l column l % 32.  A load whose
+    // lane l the granule that belongs at position l of that row.  x: load q of
+    // the wave fills rows 2 j and 2 j + 1 (j = wave + 4 q) of the stage's x
+    // rows (8 granules each), lane l column l % 32.  A load whose
     // row lies past the chunk (or past K), or whose column lies past N, gets
     // an offset no buffer reaches and writes zeros; each limit below is the
     // first stage row offset k0 at which that happens.
@@ -160,10 +166,14 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
     int w_kend[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) w_kend[j] = w_col[j & 3] >= 0 ? k_limit - (8 * wave + j) : INT_MIN;
-    const int xm = 2 * wave + (lane >> 5);
     const int xk = lane & 31;
-    const int x_kend = xm < M ? k_limit - xk : INT_MIN;
-    const int x_off = xm < M ? (int)((xm * g.ldx + xk) * 4) : 0;
+    int x_kend[G], x_off[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int xm = 2 * (wave + 4 * q) + (lane >> 5);
+        x_kend[q] = xm < M ? k_limit - xk : INT_MIN;
+        x_off[q] = xm < M ? (int)((xm * g.ldx + xk) * 4) : 0;
+    }
 
     auto issue = [&](auto buf_tag, int s) {
         constexpr int B = decltype(buf_tag)::value;
@@ -176,16 +186,20 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(buf + r * kRowSlots), 16, o, 0, 0,
                                                      kStreamAux);
         }
-        const int ox = k0 < x_kend ? x_off + 4 * k0 : kNoOffset;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(xring<B>() + 16 * wave), 4, ox, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int ox = k0 < x_kend[q] ? x_off[q] + 4 * k0 : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(xring<B>() + 16 * (wave + 4 * q)), 4,
+                                                     ox, 0, 0, 0);
+        }
     };
 
-    // Fragment addresses.  A: lane l is row i = l % 16 (x row i / 2, hi for
-    // even i, lo for odd i) and k = 8 (l / 16) + e.  B (two transposed reads
-    // of 4 rows each): lane l's column is 128 wave + 16 t + l % 16.
+    // Fragment addresses.  A (group q of 8 x rows): lane l is row i = l % 16
+    // (x row 8 q + i / 2, hi for even i, lo for odd i) and k = 8 (l / 16) + e.
+    // B (two transposed reads of 4 rows each): lane l's column is
+    // 128 wave + 16 t + l % 16; each B fragment serves every group.
     const int ai = lane & 15;
     const int am = ai >> 1;
-    const bool a_live = am < M;
     const bool a_lo = ai & 1;
     const int kq = lane >> 4;
     const int j4 = (lane & 15) >> 2;
@@ -193,21 +207,14 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
     const int b_col = 16 * wave + ((lane & 3) >> 1);  // granule, + 2 t
     const int b_half = (lane & 1) * 8;                // byte within the granule
 
-    floatx4_t acc[8];
+    floatx4_t acc[G][8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = floatx4_t{};
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[q][t] = floatx4_t{};
 
     auto compute = [&](const uint4 *buf, const uint4 *xb) {
-        // x[am][8 kq .. 8 kq + 7] (rows of 32 floats = 8 granules).
-        const floatx4_t x0 = __builtin_bit_cast(floatx4_t, xb[am * 8 + 2 * kq]);
-        const floatx4_t x1 = __builtin_bit_cast(floatx4_t, xb[am * 8 + 2 * kq + 1]);
-        half8_t a;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            _Float16 h, l;
-            split_value(e < 4 ? x0[e] : x1[e - 4], h, l);
-            a[e] = a_live ? (a_lo ? l : h) : (_Float16)0.0f;
-        }
+        half8_t b[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             short4_t v[2];
@@ -217,8 +224,26 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
                 const int byte = w_slot(r, b_col + 2 * t) * 16 + b_half;
                 v[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((CFP32_LDS short4_t *)((CFP32_LDS char *)buf + byte));
             }
-            const short8_t b = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, b), acc[t], 0, 0, 0);
+            const short8_t bv = {v[0][0], v[0][1], v[0][2], v[0][3], v[1][0], v[1][1], v[1][2], v[1][3]};
+            b[t] = __builtin_bit_cast(half8_t, bv);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            // x[8 q + am][8 kq .. 8 kq + 7] (rows of 32 floats = 8 granules).
+            const int row = 8 * q + am;
+            const floatx4_t x0 = __builtin_bit_cast(floatx4_t, xb[row * 8 + 2 * kq]);
+            const floatx4_t x1 = __builtin_bit_cast(floatx4_t, xb[row * 8 + 2 * kq + 1]);
+            const bool live = row < M;
+            half8_t a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                _Float16 h, l;
+                split_value(e < 4 ? x0[e] : x1[e - 4], h, l);
+                a[e] = live ? (a_lo ? l : h) : (_Float16)0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[t], acc[q][t], 0, 0, 0);
         }
     };
 
@@ -253,16 +278,19 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing zero loads land before the block exits
 
     // 16x16 accumulator layout: lane l holds column l % 16, rows 4 (l / 16) + e.
-    // Rows 4 (l / 16) + 0, 1 are hi, lo of x row 2 (l / 16); + 2, 3 of the next.
+    // Rows 4 (l / 16) + 0, 1 are hi, lo of x row 8 grp + 2 (l / 16); + 2, 3 of
+    // the next.
     const int64_t col0 = n0 + 128 * wave + (lane & 15);
 #pragma unroll
+    for (int grp = 0; grp < G; ++grp)
+#pragma unroll
     for (int q = 0; q < 2; ++q) {
-        const int m = 2 * kq + q;
+        const int m = 8 * grp + 2 * kq + q;
         if (m >= M) continue;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int64_t n = col0 + 16 * t;
-            const float ch = acc[t][2 * q], cl = acc[t][2 * q + 1];
+            const float ch = acc[grp][t][2 * q], cl = acc[grp][t][2 * q + 1];
             if (g.chunks == 1 && !g.geglu) {
                 if (n < g.N) {
                     float v = merge_value(ch, cl);
@@ -400,8 +428,12 @@ hipError_t launch_product(const GemvArgs &g, int64_t blocks, hipStream_t stream)
         gemv_valu_kernel<1><<<dim3((unsigned)blocks), kValuThreads, 0, stream>>>(g);
     else if (g.M == 2)
         gemv_valu_kernel<2><<<dim3((unsigned)blocks), kValuThreads, 0, stream>>>(g);
+    else if (g.M <= 8)
+        gemv_mfma_kernel<1><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    else if (g.M <= 16)
+        gemv_mfma_kernel<2><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
-        gemv_mfma_kernel<<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -755,7 +787,7 @@ hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
 {
     GemvPlan p{};
-    if (M <= 0 || M > kGemvMaxRows || N <= 0 || K <= 0) return p;
+    if (M <= 0 || M > kGemvMaxRowsKN || N <= 0 || K <= 0) return p;
     const int64_t ntiles = tiles_of(N);
     if (ntiles > ((int64_t)1 << 40)) return p;  // keeps the byte count below in range
     p.stages = (K + kBK - 1) / kBK;
@@ -769,6 +801,9 @@ GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
             break;
         }
     if (chunks > p.stages) chunks = p.stages;
+    // Above 8 rows the partial sums (8 M N bytes per chunk, written and read
+    // back) are kept within a quarter of W's 2 K N bytes.
+    if (M > kGemvMaxRows && chunks > K / (16 * M)) chunks = K / (16 * M);
     if (chunks < 1) chunks = 1;
     p.chunks = chunks;
     p.n_pad = ntiles * kTileN;
@@ -780,7 +815,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
                        int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
                        const float *bias, bool geglu_rmw)
 {
-    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    if (M < 1 || M > kGemvMaxRowsKN || (geglu_rmw && M > kGemvMaxRows)) return hipErrorInvalidValue;
     const GemvPlan p = gemv_plan(M, N, K);
     if (!geglu_rmw && p.chunks > 0 && buffer_path_ok(x, ldx, w, ldw, M, K) &&
         (p.workspace_bytes == 0 || (part && part_bytes >= p.workspace_bytes))) {
@@ -795,6 +830,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
                                                                                      N, y, ldy, bias);
         return hipGetLastError();
     }
+    if (M > kGemvMaxRows) return hipErrorNotSupported;  // the GEMM path takes it
     switch (M) {
     case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
     case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);

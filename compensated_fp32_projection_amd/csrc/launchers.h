@@ -97,12 +97,17 @@ hipError_t launch_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *pos, 
                              float *v, int64_t T, int64_t H, int64_t D, hipStream_t stream);
 
 constexpr int64_t kGemvMaxRows = 8;
+// [K, N] weights: the small-M product and merge dispatches also take 8 < M
+// <= 16 (two groups of 8 rows of x share every W fragment; at 1 x 4096 x
+// 14336 M = 9 / 16 take 25.7 / 28.0 us against 35 / 36 us for split K,
+// while four groups, M = 32, took 42 us against 40).
+constexpr int64_t kGemvMaxRowsKN = 16;
 
 // Small-M path for W given as [N, K] (ldw >= K): one dispatch, no workspace.
 hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias = nullptr);
 
-// Small-M (1 <= M <= 8) path: K is cut into `chunks` row chunks of whole
+// Small-M (1 <= M <= 16) path: K is cut into `chunks` row chunks of whole
 // stages (`stages` = ceil(K / 32) in all); with chunks > 1 the product
 // dispatch writes per-chunk FP32 partial sums of C_hi and C_lo
 // ([chunks][M][2][n_pad] floats, workspace_bytes in all) that the merge
@@ -116,10 +121,12 @@ struct GemvPlan {
 };
 GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K);
 
-// Split + both products + merge for 1 <= M <= 8, K >= 0.  `part` (16-byte
+// Split + both products + merge for 1 <= M <= 16, K >= 0.  `part` (16-byte
 // aligned, part_bytes long) holds the partial sums.  When W does not allow
 // 16-byte buffer loads, or `part` is needed but missing or too small, one
-// fused generic kernel runs instead and `part` is not touched.
+// fused generic kernel runs instead for M <= 8 and `part` is not touched;
+// for M > 8 nothing is enqueued and hipErrorNotSupported is returned.
+// geglu_rmw needs M <= 8.
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
                        int64_t ldy, int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes,
                        hipStream_t stream, const float *bias = nullptr, bool geglu_rmw = false);

@@ -22,10 +22,12 @@
  * The guide runs the split and the merge as one dispatch each; these calls
  * map onto that: cfp32_split, cfp32_gemm (two products sharing each W tile,
  * merge fused into its epilogue) and cfp32_merge, plus cfp32_linear, which
- * runs the whole projection in one or two dispatches (for M <= 8 the split
- * is done in registers by the product dispatch and a second one reduces the
- * per-chunk partial sums and merges; for M > 8 the split is a dispatch of its
- * own or, where that is faster, is done by the GEMM as it loads x).
+ * runs the whole projection in one to three dispatches (for M <= 8, and
+ * M <= 16 with 16-byte aligned W, the split is done in registers by the
+ * product dispatch and a second one reduces the per-chunk partial sums and
+ * merges; otherwise the split is a dispatch of its own or, where that is
+ * faster, is done by the GEMM as it loads x; small grids split K and add a
+ * merge dispatch).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -138,7 +140,9 @@ CFP32_API cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t
  * is needed: an empty problem, M, N or K == 0).  Returns 0 for negative
  * sizes.  M <= 8: about chunks * M * N * 8 bytes of FP32 partial sums, with
  * at most 256 chunks (1 MiB for M = 1, N = 14336, K = 4096).
- * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes. */
+ * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes, plus, for
+ * M <= 64 on small grids, FP32 partial sums of split K (at most a quarter
+ * of W's bytes); for M <= 16 at least the small-M partial sums. */
 CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* The whole projection y = x W (guide: compensated-FP32 paragraph; small
@@ -155,12 +159,16 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         kernel that sums the chunks in order and merges (two launches).
  *         W that is not 16-byte aligned with ldw % 8 == 0 takes one fused
  *         kernel instead, which leaves the workspace untouched.
- * M  > 8: cfp32_split into the workspace, then cfp32_gemm with the merged
- *         epilogue (two launches); or, for N <= 4096 with at least 128
- *         output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0, ldw % 8 == 0,
- *         x and w 16-byte aligned, one GEMM launch that splits x on the way
- *         into LDS (the workspace is then not touched).  Both give identical
- *         bits.
+ * 8 < M <= 16 with W 16-byte aligned and ldw % 8 == 0: the same two
+ *         launches, two groups of 8 rows of x sharing every W fragment.
+ * M  > 8 otherwise: cfp32_split into the workspace, then cfp32_gemm with
+ *         the merged epilogue (two launches); or, for N <= 4096 with at
+ *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
+ *         ldw % 8 == 0, x and w 16-byte aligned, one GEMM launch that splits
+ *         x on the way into LDS (the workspace is then not touched; both give
+ *         identical bits); or, for M <= 64 with fewer than 128 tiles and
+ *         K % 8 == 0, the split, a GEMM over chunks of K writing FP32 partial
+ *         sums into the workspace, and a merge dispatch (three launches).
  * Every path sums in a fixed order: results repeat bit for bit.
  * Results satisfy |y - y_exact| <= 1e-5 * sum_k |x_k w_k| for inputs within
  * the split's domain (|x| < 65520). */
@@ -191,6 +199,8 @@ CFP32_API size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K
  *              cfp32_linear_ex_workspace_bytes(M, N, K, w_layout).
  * With CFP32_W_KN and no bias this is exactly cfp32_linear (same kernels,
  * same bits); without the bias, y equals the bias-free call to the bit.
+ * CFP32_W_NK runs the GEMM paths for every M > 8 (no small-M dispatches
+ * above 8 rows); for M > 16 both layouts give the same bits.
  * Unknown layouts give CFP32_ERR_INVALID_VALUE. */
 CFP32_API cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int w_layout,
                              const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,

@@ -82,8 +82,8 @@ def test_bias_with_k_zero():
 
 @pytest.mark.parametrize("M,K,N", [(40, 256, 300), (8192, 512, 512), (2048, 1024, 4608), (300, 1000, 777),
                                    (4100, 64, 8200)])
-def test_nk_matches_kn_bitwise_above_8_rows(M, K, N):
-    """M > 8: [N, K] weights reach the same tiles with the same k order."""
+def test_nk_matches_kn_bitwise_above_16_rows(M, K, N):
+    """M > 16: [N, K] weights reach the same tiles with the same k order."""
     A, W = workloads.random_case(M * 5 + K + N, M, K, N, a_scale=10.0)
     note(f"linear_ex nk vs kn {M}x{K}x{N}")
     y_kn = run_ex(A, W, cf.W_KN)

@@ -1,14 +1,16 @@
-"""GPU tests of the split-K path of cfp32_linear / cfp32_linear_ex: 8 < M <=
-64 with fewer than 128 output tiles of 128 x 256 and K % 8 == 0 (batched
-decode shapes).  K is cut into chunks of 64-deep units, each chunk's C_hi, C_lo go
-to FP32 partial sums, and a merge dispatch adds them in chunk order and
-merges once.  The plan depends on M, N, K only, so:
-  * y is within 1e-5 * sum|a w| of the FP64 reference and finite;
-  * y's error is at least 16x below that of the single-FP16 product;
-  * repeated calls give identical bits;
-  * the LDS-DMA kernel (aligned W) and the generic kernel (unaligned W) give
-    identical bits, and so do [K, N] and [N, K] weights;
-  * the bias is one more FP32 addition after the merge.
+"""GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
+(8 < M <= 64, fewer than 128 output tiles of 128 x 256):
+  * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
+    units, each chunk's C_hi, C_lo go to FP32 partial sums, and a merge
+    dispatch adds them in chunk order and merges once.  The plan depends on
+    M, N, K only, so the LDS-DMA kernel ([N, K] weights, or aligned [K, N]
+    ones for M > 16) and the generic kernel (unaligned [K, N]) give identical
+    bits;
+  * [K, N] weights with M <= 16 that allow 16-byte loads: the small-M product
+    and merge dispatches with two groups of 8 rows of x.
+Each: y is finite and within 1e-5 * sum|a w| of the FP64 reference, its
+error at least 16x below that of the single-FP16 product, repeated calls give
+identical bits, and the bias is one more FP32 addition after the merge.
 """
 import numpy as np
 import pytest
@@ -47,6 +49,13 @@ def planes_bytes(M, K):
     return 2 * ((M * ld * 2 + 255) // 256 * 256)
 
 
+def check(y, A, W, what):
+    y64, abs64 = oracle.y64(A, W)
+    assert_within_tolerance(y, y64, abs64, what)
+    _, ch, _ = oracle.linear_cf32(A[:16], W)
+    assert_better_than_single(y[:16], ch, y64[:16], abs64[:16], what)
+
+
 # (M, K, N): the smallest M of the GEMM path, ragged N and K; many chunks;
 # the batched-decode FFN shape at the largest M that splits; a ragged last
 # unit of K; a chunk count that is not a power of two.
@@ -54,39 +63,49 @@ SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), 
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
-def test_split_k_against_reference(M, K, N):
-    need = cf.cfp32_linear_workspace_bytes(M, N, K)
+def test_split_k_against_reference_and_across_kernels(M, K, N):
+    """[N, K] weights (LDS-DMA kernel) and unaligned [K, N] weights (generic
+    kernel) cut K at the same places: the same bits, within tolerance."""
+    need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
     assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
     A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
     note(f"split-K {M}x{K}x{N}")
+    y_nk = run(A, W, layout=cf.W_NK)
+    check(y_nk, A, W, f"split-K {M}x{K}x{N}")
+    y_gen = run(A, W, w_offset=1)
+    assert np.array_equal(y_nk.view(np.uint32), y_gen.view(np.uint32))
+    if M > 16:  # aligned [K, N]: the LDS-DMA kernel as well
+        y_dma = run(A, W)
+        assert np.array_equal(y_nk.view(np.uint32), y_dma.view(np.uint32))
+    y2 = run(A, W, layout=cf.W_NK)
+    assert np.array_equal(y_nk.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+
+
+# (M, K, N): ragged M inside the second group of 8 rows, ragged N and K, the
+# batched-decode FFN shape, one chunk (many tiles).
+WIDE = [(9, 1000, 776), (16, 4096, 14336), (13, 333, 1000), (12, 64, 140000), (16, 4100, 2048)]
+
+
+@pytest.mark.parametrize("M,K,N", WIDE)
+def test_small_m_groups_against_reference(M, K, N):
+    A, W = workloads.random_case(M * 11 + K + 3 * N, M, K, N, a_scale=20.0)
+    note(f"small-M groups {M}x{K}x{N}")
     y = run(A, W)
-    rows = np.arange(M)
-    y64, abs64 = oracle.y64(A[rows], W)
-    assert_within_tolerance(y[rows], y64, abs64, f"split-K {M}x{K}x{N}")
-    _, ch, _ = oracle.linear_cf32(A[rows[:16]], W)
-    assert_better_than_single(y[rows[:16]], ch, y64[:16], abs64[:16], f"split-K {M}x{K}x{N}")
+    if N > 20000:  # the FP64 reference on a column sample
+        cols = np.random.default_rng(N).choice(N, 2048, replace=False)
+        check(y[:, cols], A, np.ascontiguousarray(W[:, cols]), f"small-M groups {M}x{K}x{N}")
+    else:
+        check(y, A, W, f"small-M groups {M}x{K}x{N}")
     y2 = run(A, W)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
 
 
-@pytest.mark.parametrize("M,K,N", [(9, 1000, 777), (40, 4104, 520), (24, 2000, 777)])
-def test_split_k_kernels_and_layouts_agree(M, K, N):
-    """Aligned [K, N] (LDS-DMA kernel), unaligned [K, N] (generic kernel) and
-    [N, K] weights: the same cuts, so the same bits."""
-    A, W = workloads.random_case(M + 3 * K + N, M, K, N, a_scale=20.0)
-    note(f"split-K kernels agree {M}x{K}x{N}")
-    y_dma = run(A, W)
-    y_gen = run(A, W, w_offset=1)
-    y_nk = run(A, W, layout=cf.W_NK)
-    assert np.array_equal(y_dma.view(np.uint32), y_gen.view(np.uint32))
-    assert np.array_equal(y_dma.view(np.uint32), y_nk.view(np.uint32))
-
-
-def test_split_k_bias_is_one_addition():
-    M, K, N = 32, 2048, 1000
-    A, W = workloads.random_case(99, M, K, N, a_scale=20.0)
+@pytest.mark.parametrize("M,K,N,layout", [(32, 2048, 1000, cf.W_NK), (24, 2048, 1000, cf.W_KN),
+                                          (16, 2048, 1000, cf.W_KN)])
+def test_bias_is_one_addition(M, K, N, layout):
+    A, W = workloads.random_case(99 + M, M, K, N, a_scale=20.0)
     bias = (np.random.default_rng(5).standard_normal(N) * 3).astype(np.float32)
-    note("split-K bias")
-    y0 = run(A, W)
-    y1 = run(A, W, bias=bias)
+    note(f"bias {M}x{K}x{N}")
+    y0 = run(A, W, layout=layout)
+    y1 = run(A, W, layout=layout, bias=bias)
     assert np.array_equal(y1.view(np.uint32), (y0 + bias[None, :]).astype(np.float32).view(np.uint32))

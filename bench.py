@@ -19,8 +19,9 @@ stream inside the timed loop give each kernel's average duration; the MFMA
 roofline is taken for the GEMM, the dominant kernel.
 
 One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
-``headline`` (the 4096^3 GEMM and the M = 1 decode path measured on their
-own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
+``headline`` (the 4096^3 GEMM, the M = 1 decode path in both weight
+layouts and captured in a graph, and batched decode at M = 16 and 64,
+each measured on its own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
 the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
 ``geglu_ffn_8192x4096x7168`` (the FFN projection with its GEGLU fused,
 next to the plain projection of the same operands),
@@ -297,6 +298,21 @@ def main():
     del Wts
     gemv_us = timed(lambda i: check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y1.data_ptr(), N_,
                                                     M_DEC, N_, K_, dec_ws.data_ptr(), dec_ws_bytes, sh), "decode"), 100)
+    # Batched decode (the rows of the prefill input, same W copies): 16 rows
+    # take the small-M dispatches, 64 the split-K GEMM.
+    batched = {}
+    for mb in (16, 64):
+        xb = x2[:mb]
+        yb = torch.empty((mb, N_), dtype=torch.float32, device=dev)
+        need_b = cf.cfp32_linear_workspace_bytes(mb, N_, K_)
+        wsb = torch.empty(max(need_b, 1), dtype=torch.uint8, device=dev)
+        us = timed(lambda i, xb=xb, yb=yb, wsb=wsb, mb=mb, need_b=need_b: check(
+            cf.cfp32_linear(xb.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, yb.data_ptr(), N_, mb, N_, K_,
+                            wsb.data_ptr(), need_b, sh), "batched decode"), 50)
+        bytes_b = K_ * N_ * 2 + mb * K_ * 4 + mb * N_ * 4
+        batched[f"linear_{mb}x4096x14336_us"] = round(us, 2)
+        batched[f"linear_{mb}x4096x14336_frac_hbm"] = round(bytes_b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        del xb, yb, wsb
     sq = workloads.square()
     xs = torch.from_numpy(sq.A[0]).to(dev)
     ws = torch.from_numpy(sq.W.view(np.int16)).to(dev)
@@ -388,6 +404,7 @@ def main():
             "gemv_graph_frac_hbm": round(dec_bytes / (gemv_graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "gemv_nk_1x4096x14336_us": round(gemv_nk_us, 2),
             "gemv_nk_frac_hbm": round(dec_bytes / (gemv_nk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            **batched,
         },
         "fp32_ab_4096": {
             "cfp32_linear_us": round(lin_us, 2),

@@ -266,7 +266,13 @@ size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_t K)
         return b == 0 ? 0 : b + kAlign;
     }
     if (!extent_ok(M, split_ld(K))) return 0;
-    return 2 * plane_bytes(M, K) + kAlign;
+    // As cfp32_linear_ex over the [K, 2F] weight: the GEMM path (planes, plus
+    // split-K partial sums on small grids), or up to 16 rows the small-M
+    // dispatches when W allows 16-byte loads.
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, 2 * F, K);
+    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
+    const size_t small_m = M <= cfp32::kGemvMaxRowsKN ? cfp32::gemv_geglu_plan(M, F, K).workspace_bytes : 0;
+    return (gemm_path > small_m ? gemm_path : small_m) + kAlign;
 }
 
 cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, const float *bias,
@@ -303,6 +309,14 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
         return launched(cfp32::launch_gemv(x, ldx, w_up, ldw, out, ldo, M, F, K, nullptr, 0, s, bias_up, true));
     }
 
+    if (M <= cfp32::kGemvMaxRowsKN && K > 0) {
+        // Up to 16 rows: the small-M product dispatch over all 2F columns and
+        // the GEGLU merge, when W allows 16-byte loads (else the GEMM path).
+        const hipError_t e = cfp32::launch_gemv_geglu(x, ldx, w, ldw, out, ldo, M, F, K,
+                                                      reinterpret_cast<float *>(base), need - kAlign, s, bias);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
+
     if (K == 0) {
         hipError_t e = cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F, 0,
                                           false, s, bias);
@@ -320,6 +334,15 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
     // (the rule of the plain GEMM: at least one 128 x 256 W tile per CU).
     if (((M + 127) / 128) * ((F + 127) / 128) >= 256) {
         e = cfp32::launch_gemm_dma_geglu(hi, lo, ldh, w, ldw, out, ldo, M, F, K, /*a_zero_padded=*/true, s, bias);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
+    // Small grids: split K over all 2F columns (the cuts cfp32_linear_ex
+    // makes for the [K, 2F] projection) and the GEGLU merge.
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, 2 * F, K);
+    if (sp.chunks > 1) {
+        float *part = reinterpret_cast<float *>(base + 2 * plane_bytes(M, K));
+        e = cfp32::launch_gemm_chunked(hi, lo, ldh, w, ldw, out, ldo, M, 2 * F, K, /*a_zero_padded=*/true, s, bias,
+                                       false, part, sp.workspace_bytes, /*geglu=*/true);
         if (e != hipErrorNotSupported) return launched(e);
     }
     e = cfp32::launch_gemm(hi, lo, ldh, w, ldw, out, ldo, nullptr, nullptr, ldo, M, F, K, true, s, bias);

@@ -546,10 +546,11 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
 hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                                int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                bool a_zero_padded, hipStream_t stream, const float *bias, bool w_nk, float *part,
-                               size_t part_bytes)
+                               size_t part_bytes, bool geglu)
 {
     const GemmSplitPlan p = gemm_split_plan(M, N, K);
-    if (p.chunks < 2 || !part || part_bytes < p.workspace_bytes) return hipErrorNotSupported;
+    if (p.chunks < 2 || !part || part_bytes < p.workspace_bytes || (geglu && (w_nk || N % 2)))
+        return hipErrorNotSupported;
     hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, nullptr, 0, nullptr, nullptr, 0, M, N, K, a_zero_padded,
                                    stream, nullptr, w_nk, p.chunks, part, p.n_pad);
     if (e == hipErrorNotSupported) {
@@ -558,6 +559,7 @@ hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64
         e = w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
     }
     if (e != hipSuccess) return e;
+    if (geglu) return launch_partial_geglu_merge(part, p.n_pad, p.chunks, M, N / 2, y, ldy, bias, stream);
     return launch_partial_merge(part, p.n_pad, p.chunks, M, N, y, ldy, bias, stream);
 }
 

@@ -774,6 +774,16 @@ hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_
 
 // About one block per CU over all column tiles; a chunk has at least one
 // stage of 32 rows.
+hipError_t launch_partial_geglu_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t F,
+                                      float *out, int64_t ldo, const float *bias, hipStream_t stream)
+{
+    const int64_t outs = M * F;
+    if (M > 0x7FFFFFFF || (outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    gemv_geglu_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, n_pad, chunks, (int)M, F,
+                                                                                       out, ldo, bias);
+    return hipGetLastError();
+}
+
 hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t N, float *y,
                                 int64_t ldy, const float *bias, hipStream_t stream)
 {
@@ -858,7 +868,7 @@ hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int
                              int64_t M, int64_t F, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
                              const float *bias)
 {
-    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    if (M < 1 || M > kGemvMaxRowsKN) return hipErrorInvalidValue;
     const GemvPlan p = gemv_geglu_plan(M, F, K);
     if (p.chunks == 0 || !buffer_path_ok(x, ldx, w, ldw, M, K) || !part || part_bytes < p.workspace_bytes)
         return hipErrorNotSupported;

@@ -67,16 +67,22 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K);
 // chunk sums, + bias).  hipErrorNotSupported, with nothing enqueued, when the
 // plan has one chunk or `part` is missing or smaller than the plan's
 // workspace.  The LDS-DMA kernel when the operands allow it, else the
-// generic kernel (same cuts, same bits).
+// generic kernel (same cuts, same bits).  geglu: W is [K, N = 2F] (gate |
+// up columns, [K, N] layout only) and y [M, F] receives gelu(gate) * up
+// from the GEGLU merge dispatch (bias [2F]).
 hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                                int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                                bool a_zero_padded, hipStream_t stream, const float *bias, bool w_nk, float *part,
-                               size_t part_bytes);
+                               size_t part_bytes, bool geglu = false);
 
 // Sum of `chunks` partial sums part[c][m][2][n_pad] in chunk order, merged
-// into y [M, N] (+ bias) (gemv.hip's merge dispatch).
+// into y [M, N] (+ bias) (gemv.hip's merge dispatch); the GEGLU form reads
+// gate column n and up column F + n and writes gelu(gate) * up to out [M, F]
+// (bias [2F]).
 hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t N, float *y,
                                 int64_t ldy, const float *bias, hipStream_t stream);
+hipError_t launch_partial_geglu_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t F,
+                                      float *out, int64_t ldo, const float *bias, hipStream_t stream);
 
 // LDS-DMA GEMM on FP32 A, split in registers (one launch for the whole
 // projection); hipErrorNotSupported, with nothing enqueued, unless K % 4 == 0,
@@ -131,7 +137,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
                        int64_t ldy, int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes,
                        hipStream_t stream, const float *bias = nullptr, bool geglu_rmw = false);
 
-// GEGLU for 1 <= M <= 8 over W [K, 2F]: out [M, F] = gelu(gate) * up.  The
+// GEGLU for 1 <= M <= 16 over W [K, 2F]: out [M, F] = gelu(gate) * up.  The
 // plan's workspace holds partial sums for all 2F columns.
 GemvPlan gemv_geglu_plan(int64_t M, int64_t F, int64_t K);
 hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *out, int64_t ldo,

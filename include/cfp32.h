@@ -223,10 +223,13 @@ CFP32_API size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_
  * cfp32_linear gives for those columns); the activation and the product run
  * in FP32 in the kernel that merges them (erff and three roundings).
  * M > 8 with at least 256 output tiles of 128 x 128 (and aligned operands):
- * the split, then one GEMM launch with the GEGLU in its epilogue.  M <= 8:
- * the small-M product dispatch over all 2F columns, then a merge dispatch
- * that forms out.  Other cases run the gate projection into out and the up
- * projection with a read-modify-write epilogue (one more launch). */
+ * the split, then one GEMM launch with the GEGLU in its epilogue.  M <= 8
+ * (M <= 16 with 16-byte aligned W, ldw % 8 == 0): the small-M product
+ * dispatch over all 2F columns, then a merge dispatch that forms out.
+ * M <= 64 on small grids with K % 8 == 0: the split, a GEMM over chunks of K
+ * into FP32 partial sums in the workspace, then that merge dispatch.  Other
+ * cases run the gate projection into out and the up projection with a
+ * read-modify-write epilogue (one more launch). */
 CFP32_API cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
                                 const float *bias, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                 void *workspace, size_t workspace_bytes, void *stream);

@@ -123,10 +123,12 @@ def test_workspace_sizes(lib):
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, cf.W_NK) == 2 * 256 + 256
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, 7) == 0
     # cfp32_linear_geglu: M <= 8 holds partial sums for all 2F columns, even
-    # for a single chunk; M > 8 the hi/lo planes.
+    # for a single chunk; M > 8 the hi/lo planes, and up to 16 rows at least
+    # those partial sums (the small-M dispatches when W allows 16-byte loads).
     assert cf.cfp32_linear_geglu_workspace_bytes(1, 7168, 4096) == 8 * 1 * 2 * 14336 * 4 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 8) == 1 * 2 * 2 * 512 * 4 + 256
-    assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 2 * 256 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 1 * 9 * 2 * 512 * 4 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(17, 5, 1) == 2 * 512 + 256  # planes of 17 x 8 FP16
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0

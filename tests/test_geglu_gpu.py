@@ -75,9 +75,12 @@ def check_geglu(out, y_full, F, what):
 
 
 # (M, K, F): small-M chunked; small-M with one stage (partials still used);
-# M = 8; M > 8 small grid (two-pass fallback); the fused GEMM epilogue
-# (>= 256 tiles of 128 x 128, ragged F and M).
-SHAPES = [(1, 4096, 1536), (3, 24, 40), (8, 1000, 520), (40, 256, 300), (2100, 512, 2000)]
+# M = 8; two groups of 8 rows in the small-M dispatch; M > 8 small grid with
+# K too short to split (two-pass fallback); split K over all 2F columns with
+# the GEGLU merge; the fused GEMM epilogue (>= 256 tiles of 128 x 128,
+# ragged F and M).
+SHAPES = [(1, 4096, 1536), (3, 24, 40), (8, 1000, 520), (13, 2048, 1000), (40, 256, 300), (48, 2048, 2000),
+          (2100, 512, 2000)]
 
 
 @pytest.mark.parametrize("with_bias", [False, True])
@@ -101,7 +104,7 @@ def test_geglu_paths(M, K, F, with_bias):
     assert_within_tolerance(y_full[rows], y64, abs64, f"projection {M}x{K}x{F}")
 
 
-@pytest.mark.parametrize("M", [2, 40])
+@pytest.mark.parametrize("M", [2, 12, 40])
 def test_geglu_unaligned_weight_fallback(M):
     K, F = 200, 96
     A, W = workloads.random_case(M * 3, M, K, 2 * F, a_scale=8.0)

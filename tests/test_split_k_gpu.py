@@ -3,11 +3,11 @@
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
     units, each chunk's C_hi, C_lo go to FP32 partial sums, and a merge
     dispatch adds them in chunk order and merges once.  The plan depends on
-    M, N, K only, so the LDS-DMA kernel ([N, K] weights, or aligned [K, N]
-    ones for M > 16) and the generic kernel (unaligned [K, N]) give identical
-    bits;
-  * [K, N] weights with M <= 16 that allow 16-byte loads: the small-M product
-    and merge dispatches with two groups of 8 rows of x.
+    M, N, K only, so the LDS-DMA kernel (aligned weights, M > 16) and the
+    generic kernel (unaligned weights) give identical bits in both layouts;
+  * [K, N] weights with M <= 16 that allow 16-byte loads: the small-M
+    product and merge dispatches with two groups of 8 rows of x ([N, K]
+    weights take split K there too).
 Each: y is finite and within 1e-5 * sum|a w| of the FP64 reference, its
 error at least 16x below that of the single-FP16 product, repeated calls give
 identical bits, and the bias is one more FP32 addition after the merge.
@@ -64,21 +64,22 @@ SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
 def test_split_k_against_reference_and_across_kernels(M, K, N):
-    """[N, K] weights (LDS-DMA kernel) and unaligned [K, N] weights (generic
-    kernel) cut K at the same places: the same bits, within tolerance."""
+    """Unaligned weights (generic kernel) in both layouts, and for M > 16
+    aligned ones (LDS-DMA kernel), cut K at the same places: the same bits,
+    within tolerance."""
     need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
     assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
     A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
     note(f"split-K {M}x{K}x{N}")
-    y_nk = run(A, W, layout=cf.W_NK)
-    check(y_nk, A, W, f"split-K {M}x{K}x{N}")
-    y_gen = run(A, W, w_offset=1)
-    assert np.array_equal(y_nk.view(np.uint32), y_gen.view(np.uint32))
-    if M > 16:  # aligned [K, N]: the LDS-DMA kernel as well
-        y_dma = run(A, W)
-        assert np.array_equal(y_nk.view(np.uint32), y_dma.view(np.uint32))
-    y2 = run(A, W, layout=cf.W_NK)
-    assert np.array_equal(y_nk.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    y = run(A, W, w_offset=1)
+    check(y, A, W, f"split-K {M}x{K}x{N}")
+    runs = [run(A, W, layout=cf.W_NK, w_offset=1)]
+    if M > 16:
+        runs += [run(A, W), run(A, W, layout=cf.W_NK)]
+    for y2 in runs:
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    y3 = run(A, W, w_offset=1)
+    assert np.array_equal(y.view(np.uint32), y3.view(np.uint32)), "not deterministic"
 
 
 # (M, K, N): ragged M inside the second group of 8 rows, ragged N and K, the
@@ -86,22 +87,23 @@ def test_split_k_against_reference_and_across_kernels(M, K, N):
 WIDE = [(9, 1000, 776), (16, 4096, 14336), (13, 333, 1000), (12, 64, 140000), (16, 4100, 2048)]
 
 
+@pytest.mark.parametrize("layout", [cf.W_KN, cf.W_NK])
 @pytest.mark.parametrize("M,K,N", WIDE)
-def test_small_m_groups_against_reference(M, K, N):
+def test_small_m_groups_against_reference(M, K, N, layout):
     A, W = workloads.random_case(M * 11 + K + 3 * N, M, K, N, a_scale=20.0)
-    note(f"small-M groups {M}x{K}x{N}")
-    y = run(A, W)
+    note(f"small-M groups {M}x{K}x{N} layout {layout}")
+    y = run(A, W, layout=layout)
     if N > 20000:  # the FP64 reference on a column sample
         cols = np.random.default_rng(N).choice(N, 2048, replace=False)
         check(y[:, cols], A, np.ascontiguousarray(W[:, cols]), f"small-M groups {M}x{K}x{N}")
     else:
         check(y, A, W, f"small-M groups {M}x{K}x{N}")
-    y2 = run(A, W)
+    y2 = run(A, W, layout=layout)
     assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
 
 
 @pytest.mark.parametrize("M,K,N,layout", [(32, 2048, 1000, cf.W_NK), (24, 2048, 1000, cf.W_KN),
-                                          (16, 2048, 1000, cf.W_KN)])
+                                          (16, 2048, 1000, cf.W_KN), (12, 2048, 1000, cf.W_NK)])
 def test_bias_is_one_addition(M, K, N, layout):
     A, W = workloads.random_case(99 + M, M, K, N, a_scale=20.0)
     bias = (np.random.default_rng(5).standard_normal(N) * 3).astype(np.float32)

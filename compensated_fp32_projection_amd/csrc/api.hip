@@ -5,7 +5,6 @@
 
 #include <atomic>
 #include <cstring>
-#include <limits>
 
 #include "../../include/cfp32.h"
 #include "launchers.h"
@@ -18,7 +17,11 @@ constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 std::atomic<int> g_arch_state[kMaxDevices];
 
-constexpr int64_t kMaxDim = std::numeric_limits<int64_t>::max() / 4;
+// Every dimension, and every rows x ld extent, stays below 2^48 elements
+// (far above any device memory): size products formed on the host and in
+// the launchers, such as (M + tile rows) * ld * 4 or chunks * M * N * 8,
+// then cannot overflow 64 bits.
+constexpr int64_t kMaxDim = ((int64_t)1 << 48) - 1;
 
 cfp32_status hip_fail(hipError_t e)
 {
@@ -52,7 +55,7 @@ cfp32_status check_device()
 
 bool dims_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && a <= kMaxDim && b <= kMaxDim; }
 
-// rows x ld elements must be addressable with 64-bit offsets.
+// rows x ld elements within the 2^48-element limit.
 bool extent_ok(int64_t rows, int64_t ld) { return rows == 0 || ld <= kMaxDim / rows; }
 
 cfp32_status launched(hipError_t e) { return e == hipSuccess ? CFP32_OK : hip_fail(e); }

@@ -42,6 +42,8 @@
  *   surface at the caller's next synchronisation.
  * - Arguments are validated before anything is enqueued.  A call that
  *   returns an error has enqueued nothing.
+ * - Every dimension, and every rows x ld extent of an operand, must be
+ *   below 2^48 elements; larger values give CFP32_ERR_INVALID_VALUE.
  * - M == 0 or N == 0 (rows == 0 or cols == 0 for split) is a no-op that
  *   returns CFP32_OK.  K == 0 writes +0 to every output element.
  * - The current HIP device must be gfx950; otherwise

@@ -92,9 +92,14 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert cf.cfp32_qkv_rotary(FAKE, 96, None, 0.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
     assert cf.cfp32_qkv_rotary(FAKE, 95, None, 10000.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
     assert cf.cfp32_qkv_rotary(None, 96, None, 10000.0, FAKE, FAKE, FAKE, 4, 2, 16, None) == E
-    # sizes whose extent overflows 64-bit offsets
+    # dimensions or rows x ld extents of 2^48 elements or more
     big = 1 << 40
     assert cf.cfp32_split(FAKE, big, FAKE, FAKE, big, big, 4, None) == E
+    assert cf.cfp32_split(FAKE, 1 << 48, FAKE, FAKE, 1 << 48, 1, 1 << 48, None) == E
+    assert cf.cfp32_gemm(FAKE, FAKE, 1 << 47, FAKE, 8, FAKE, None, None, 8, 2, 8, 8, None) == E
+    assert cf.cfp32_gemm(FAKE, FAKE, 8, FAKE, 8, FAKE, None, None, 8, 2, 8, 1 << 48, None) == E
+    assert cf.cfp32_linear(FAKE, (1 << 47) + 8, FAKE, 8, FAKE, 8, 2, 8, 8, FAKE, 1 << 20, None) == E
+    assert cf.cfp32_merge(FAKE, FAKE, 1 << 46, FAKE, 8, 4, 8, None) == E
 
 
 def test_workspace_sizes(lib):

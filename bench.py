@@ -27,8 +27,10 @@ the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
 next to the plain projection of the same operands),
 ``separate_add_4096`` (the separate-addition accumulation mode at 4096^3,
 k_per_add 0 = plain accumulation in the same kernel configuration),
-``roofline`` and ``cpu_baseline`` (the CPU oracle timed on a bounded sample
-of the same workload on this host).
+``roofline``, ``rocprof_mfma`` (the GEMM's matrix-unit utilisation and
+shader clock as rocprofv3 counters measured them, from the committed summary
+while the GEMM source is unchanged) and ``cpu_baseline`` (the CPU oracle
+timed on a bounded sample of the same workload on this host).
 """
 from __future__ import annotations
 
@@ -143,6 +145,86 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
     print("\n".join(lines))
 
 
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mfma_utilisation_counters.txt")
+# grid sizes (threads) of the plain GEMM launches in a bench run -> (M, K, N)
+GEMM_GRIDS = {1835008: (8192, 4096, 14336), 262144: (4096, 4096, 4096)}
+
+
+def summarize_mfma(csv_path, out_path, command):
+    """Write the matrix-unit summary of the GEMM launches from one rocprofv3
+    --pmc run of MfmaUtil (rocprofv3's derived metric: the summed
+    SQ_VALU_MFMA_BUSY_CYCLES over the largest per-XCD GRBM_GUI_ACTIVE times
+    the SIMD count), SQ_INSTS_VALU_MFMA_MOPS_F16 (FP16 MFMA operations / 512)
+    and GRBM_GUI_ACTIVE, with each dispatch's start and end timestamps.  The
+    clock follows from the active cycles of one XCD over the duration."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if GEMM_KERNEL not in r["Kernel_Name"]:
+                continue
+            grid = int(r.get("Grid_Size", 0) or 0)
+            if grid not in GEMM_GRIDS:
+                continue
+            d = per.setdefault((grid, r["Dispatch_Id"]), {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    lines = ["# rocprofv3 counter summary: dual-product GEMM matrix-unit utilisation and clock, MI355X",
+             f"# command: {command}",
+             f"kernel_source_hash: {kernel_source_hash()}"]
+    simds = 256 * 4
+    for grid, (M, K, N) in GEMM_GRIDS.items():
+        ds = [v for (g, _), v in per.items() if g == grid and "MfmaUtil" in v and "SQ_VALU_MFMA_BUSY_CYCLES" in v]
+        if not ds:
+            raise SystemExit(f"{csv_path}: no MfmaUtil rows for the {M}x{K}x{N} GEMM")
+        n = len(ds)
+        util = sum(v["MfmaUtil"] for v in ds) / n
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in ds) / n
+        dur_us = sum(v["dur_ns"] for v in ds) / n / 1e3
+        # the largest per-XCD active-cycle count, recovered from the derived metric
+        active = busy / (util / 100.0 * simds)
+        clock = active / (dur_us * 1e3)
+        flops = sum(v["SQ_INSTS_VALU_MFMA_MOPS_F16"] for v in ds) / n * 512
+        alg = 4.0 * M * N * K
+        rate = alg / (dur_us * 1e-6) / 1e12
+        at_clock = 256 * 4096 * clock * 1e9 / 1e12
+        tag = f"gemm_{M}x{K}x{N}"
+        lines += [f"{tag}_dispatches: {n}",
+                  f"{tag}_MfmaUtil_percent: {util:.2f}",
+                  f"{tag}_mfma_busy_cycles_per_simd: {busy / simds:.4e}",
+                  f"{tag}_active_cycles_per_xcd: {active:.4e}",
+                  f"{tag}_duration_us_under_counters: {dur_us:.1f}",
+                  f"{tag}_clock_GHz: {clock:.3f}",
+                  f"{tag}_fp16_mfma_flops_counted: {flops:.4e}  (algorithmic 4MNK: {alg:.4e}, ratio {flops / alg:.4f})",
+                  f"{tag}_TFLOPs: {rate:.1f}  ({100 * rate / PEAK_FP16_TFLOPS:.1f}% of the 2.4 GHz peak, "
+                  f"{100 * rate / at_clock:.1f}% of the peak at {clock:.3f} GHz)"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_mfma():
+    """MfmaUtil and clock of the 8192 x 4096 x 14336 GEMM from the committed
+    rocprofv3 summary, or None when there is none or the GEMM source has
+    changed since."""
+    try:
+        text = open(MFMA_SUMMARY).read()
+    except OSError:
+        return None
+    src = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    if not src or src.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    for key, pat in (("mfma_util", r"^gemm_8192x4096x14336_MfmaUtil_percent:\s*([0-9.]+)"),
+                     ("clock_ghz", r"^gemm_8192x4096x14336_clock_GHz:\s*([0-9.]+)")):
+        m = re.search(pat, text, re.M)
+        if not m:
+            return None
+        out[key] = float(m.group(1))
+    out["mfma_util"] = round(out["mfma_util"] / 100.0, 4)
+    out["source"] = "profiles/gemm_mfma_utilisation_counters.txt (rocprofv3 MfmaUtil, GRBM_GUI_ACTIVE)"
+    return out
+
+
 def summarize_trace(trace_csv, out_path, command):
     """Write per-kernel, per-grid-size durations from a rocprofv3
     --kernel-trace run (its *_kernel_trace.csv): one line per distinct
@@ -180,12 +262,18 @@ def main():
                     help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_CSV", "OUT"),
+                    help="summarise a rocprofv3 --pmc run of MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_F16 and "
+                         "GRBM_GUI_ACTIVE (no GPU needed)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "OUT"),
                     help="summarise a rocprofv3 --kernel-trace run, its *_kernel_trace.csv (no GPU needed)")
     ap.add_argument("--profile-command", default="", help="command line recorded in the summary")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.profile_command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.profile_command)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.profile_command)
@@ -384,6 +472,7 @@ def main():
                      "achieved": round(gemm_tf16, 1), "peak": round(PEAK_FP16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(gemm_tf16 / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic},
+        "rocprof_mfma": measured_mfma(),
         "breakdown": {
             "decode_gemv_us": round(dec_us, 2),
             "decode_gemv_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),

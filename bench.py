@@ -145,6 +145,91 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
     print("\n".join(lines))
 
 
+GEMV_SUMMARY = os.path.join(ROOT, "profiles", "decode_gemv_1x4096x14336_counters.txt")
+GEMV_PRODUCT_KERNEL = "gemv_valu_kernel<1>"  # the M = 1 product dispatch
+GEMV_MERGE_KERNEL = "gemv_merge_kernel"
+GEMV_GRID = 14336                            # threads of the M = 1 merge dispatch
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("gemv.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def summarize_gemv_counters(fetch_csv, write_csv, out_path, command):
+    """Write the HBM-traffic summary of the M = 1 decode path (product and
+    merge dispatches) from the same two rocprofv3 --pmc runs as the GEMM's,
+    each counter scaled by what it reads for the plain copy of CALIB_BYTES;
+    the rate uses the dispatch timestamps of those runs."""
+    import csv
+    lines = ["# rocprofv3 counter summary: decode projection 1x4096x14336 (small-M product + merge dispatches)",
+             f"# command: {command}",
+             f"kernel_source_hash: {gemv_source_hash()}"]
+    result = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        prod, merge, copy = [], [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != name:
+                    continue
+                v = float(r["Counter_Value"])
+                dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                k = r["Kernel_Name"]
+                if GEMV_PRODUCT_KERNEL in k:
+                    prod.append((v, dur))
+                elif GEMV_MERGE_KERNEL in k and int(r.get("Grid_Size", 0) or 0) == GEMV_GRID:
+                    merge.append((v, dur))
+                elif COPY_KERNEL_HINT in k.lower() and v * 1024 > CALIB_BYTES * 0.5:
+                    copy.append(v)
+        if not prod or not merge or not copy:
+            raise SystemExit(f"{path}: no {name} rows for the decode dispatches or the calibration copy")
+        factor = CALIB_BYTES / (max(copy) * 1024.0)
+        for tag, rows in (("product", prod), ("merge", merge)):
+            kib = sum(v for v, _ in rows) / len(rows)
+            us = sum(d for _, d in rows) / len(rows) / 1e3
+            result[(tag, name)] = (kib * 1024.0 * factor, us)
+            lines.append(f"{tag}_{name}_KiB_per_dispatch: {kib:.1f}  (dispatches: {len(rows)}, scale {factor:.4f})")
+    alg = 4096 * 14336 * 2 + 4096 * 4
+    pb = result[("product", "FETCH_SIZE")][0] + result[("product", "WRITE_SIZE")][0]
+    pus = result[("product", "FETCH_SIZE")][1]
+    lines += [f"product_hbm_bytes_per_dispatch: {pb:.4e}",
+              f"product_read_over_algorithmic: {result[('product', 'FETCH_SIZE')][0] / alg:.4f}  (W + x = {alg} bytes)",
+              f"product_duration_us_under_counters: {pus:.2f}",
+              f"product_hbm_GBps: {pb / (pus * 1e-6) / 1e9:.1f}  "
+              f"({100 * pb / (pus * 1e-6) / 1e9 / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f} GB/s)",
+              f"merge_hbm_bytes_per_dispatch: "
+              f"{result[('merge', 'FETCH_SIZE')][0] + result[('merge', 'WRITE_SIZE')][0]:.4e}",
+              f"merge_duration_us_under_counters: {result[('merge', 'FETCH_SIZE')][1]:.2f}"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def measured_gemv():
+    """HBM figures of the M = 1 product dispatch from the committed rocprofv3
+    summary, or None when there is none or the small-M source has changed."""
+    try:
+        text = open(GEMV_SUMMARY).read()
+    except OSError:
+        return None
+    src = re.search(r"^kernel_source_hash:\s*(\S+)", text, re.M)
+    if not src or src.group(1) != gemv_source_hash():
+        return None
+    out = {}
+    for key, pat in (("hbm_bytes_per_dispatch", r"^product_hbm_bytes_per_dispatch:\s*([0-9.eE+]+)"),
+                     ("read_over_algorithmic", r"^product_read_over_algorithmic:\s*([0-9.]+)"),
+                     ("hbm_GBps", r"^product_hbm_GBps:\s*([0-9.]+)")):
+        m = re.search(pat, text, re.M)
+        if not m:
+            return None
+        out[key] = float(m.group(1))
+    out["source"] = "profiles/decode_gemv_1x4096x14336_counters.txt (rocprofv3 FETCH_SIZE, WRITE_SIZE)"
+    return out
+
+
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_mfma_utilisation_counters.txt")
 # grid sizes (threads) of the plain GEMM launches in a bench run -> (M, K, N)
 GEMM_GRIDS = {1835008: (8192, 4096, 14336), 262144: (4096, 4096, 4096)}
@@ -262,6 +347,8 @@ def main():
                     help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
                     help="summarise two rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--summarize-gemv-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
+                    help="summarise the decode dispatches of the two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_CSV", "OUT"),
                     help="summarise a rocprofv3 --pmc run of MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_F16 and "
                          "GRBM_GUI_ACTIVE (no GPU needed)")
@@ -271,6 +358,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters, args.profile_command)
+        return
+    if args.summarize_gemv_counters:
+        summarize_gemv_counters(*args.summarize_gemv_counters, args.profile_command)
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.profile_command)
@@ -473,6 +563,7 @@ def main():
                      "frac": round(gemm_tf16 / PEAK_FP16_TFLOPS, 4),
                      "traffic": traffic},
         "rocprof_mfma": measured_mfma(),
+        "rocprof_decode_gemv": measured_gemv(),
         "breakdown": {
             "decode_gemv_us": round(dec_us, 2),
             "decode_gemv_GBps": round(dec_bytes / (dec_us * 1e-6) / 1e9, 1),

@@ -186,9 +186,18 @@ __device__ __forceinline__ int a32_slot(int row, int g) { return row * 8 + (g ^ 
 // columns in its second, so one lane holds the gate and up of the same
 // output and applies the activation there.  Products, k order and merge are
 // those of the plain GEMM.
-template <bool SPLIT, bool WNK, bool GEGLU = false>
+//
+// STACK = true (split K with M <= 64 only): the block's 128 rows hold the hi
+// rows of x (rows 0-63, wave row 0) and its lo rows (rows 64-127, wave row
+// 1), and each wave runs one product, C = [A_hi; A_lo] W, instead of two
+// products over mostly empty rows.  Every accumulator sums the same
+// products in the same k order as in the two-product form, so the partial
+// sums are the same bits; wave row 0 writes them as C_hi, wave row 1 as C_lo.
+template <bool SPLIT, bool WNK, bool GEGLU = false, bool STACK = false>
 __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
+    static_assert(!STACK || (!SPLIT && !GEGLU && WTM == 64 && BM == 2 * WTM), "STACK: two wave rows, hi then lo");
+    constexpr int LPW = STACK ? LOADS_PER_WAVE - 1 : LOADS_PER_WAVE;  // STACK: one A load per wave
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: barriers branch on it
@@ -252,8 +261,11 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         const int slot = 64 * wave + lane;
         const int row = slot / KG;
         const int kg = (slot % KG) ^ ((row >> 2) & 3);
-        const bool ok = m0 + row < g.M;
-        a_off[0] = ok ? (int)(((m0 + row) * g.lda + 8 * kg) * 2) : kNoOffset;
+        // STACK (one tile row, m0 = 0): block row r holds x row r % 64 of the
+        // hi plane (waves 0-3) or the lo plane (waves 4-7).
+        const int64_t xrow = STACK ? (int64_t)(row & 63) : m0 + row;
+        const bool ok = xrow < g.M;
+        a_off[0] = ok ? (int)((xrow * g.lda + 8 * kg) * 2) : kNoOffset;
         a_kend[0] = ok ? (int)(ka_stop - 8 * kg) : 0;  // stage k0 reads this granule while k0 < a_kend
         a_off[1] = a_off[0];
         a_kend[1] = a_kend[0];
@@ -299,9 +311,14 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             }
         } else {
             const int a = k0 < a_kend[0] ? a_off[0] + 2 * k0 : kNoOffset;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0,
-                                                     0);
+            if constexpr (STACK) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(group == 0 ? rs_hi : rs_lo, (CFP32_LDS void *)(s + 64 * wave),
+                                                         16, a, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0,
+                                                         0, 0);
+            }
         }
         const int wstep = WNK ? 2 * k0 : (int)(k0_64 * g.ldw * 2);
 #pragma unroll
@@ -337,7 +354,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         for (int i = 0; i < TM; ++i) {
             const int row = a_row0 + 16 * i;
             f.ah[i] = __builtin_bit_cast(half8_t, sa[a_slot(0, row, a_kg)]);
-            f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, a_kg)]);
+            if constexpr (!STACK) f.al[i] = __builtin_bit_cast(half8_t, sa[a_slot(1, row, a_kg)]);
         }
     };
     auto read_frags = [&](const uint4 *s, const uint4 *sa, Frags &f) {
@@ -370,9 +387,11 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc_hi[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
+            if constexpr (!STACK) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
+                for (int j = 0; j < TN; ++j)
+                    acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
+            }
         }
     };
 
@@ -409,7 +428,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         __builtin_amdgcn_sched_barrier(0);
         issue(std::integral_constant<int, (S + 3) & 3>{}, (s + 3) * BK);
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LPW));
         block_barrier();
         __builtin_amdgcn_s_setprio(1);
         mfmas(f0);
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             // Stage s + 1 landed (this group's loads) before the barrier above.
             convert(stage_buf<(S + 1) & 3>(), conv_buf<(S + 1) & 1>());
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));  // the conversion's LDS writes are done
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LPW));  // the conversion's LDS writes are done
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -427,12 +446,12 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     issue(std::integral_constant<int, 0>{}, s_begin * BK);
     issue(std::integral_constant<int, 1>{}, (s_begin + 1) * BK);
     issue(std::integral_constant<int, 2>{}, (s_begin + 2) * BK);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LOADS_PER_WAVE));  // stage 0 landed for this wave
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));  // stage 0 landed for this wave
     block_barrier();
     if constexpr (SPLIT) {
         convert(stage_buf<0>(), conv_buf<0>());
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LOADS_PER_WAVE));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * LPW));
         block_barrier();
     }
     if (group == 1) block_barrier();  // the second group runs one phase behind
@@ -471,6 +490,24 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
                 __builtin_nontemporal_store(gelu_value(gate) * up, g.y + row * g.ldy + col);
             }
         }
+        return;
+    }
+    if constexpr (STACK) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = n0 + wn * WTN + j * 16 + (lane & 15);
+                if (col >= g.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t xrow = i * 16 + 4 * (lane >> 4) + e;
+                    if (xrow >= g.M) continue;
+                    // wave row 0: C_hi, wave row 1: C_lo (at + n_pad)
+                    __builtin_nontemporal_store(acc_hi[i][j][e],
+                                                g.part + ((chunk * g.M + xrow) * 2 + wm) * g.n_pad + col);
+                }
+            }
         return;
     }
 #pragma unroll
@@ -537,8 +574,15 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
     const int64_t blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN) * kchunks;
     if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
     DmaArgs g{a_hi, a_lo, nullptr, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, Ka, bias, 0, kchunks, part, n_pad};
-    if (w_nk)
+    // Split K over at most 64 rows: the hi and lo rows stacked into one tile
+    // (8 x 4096 x 14336 .. 64 x 4096 x 14336: half the matrix-unit work).
+    const bool stack = kchunks > 1 && 2 * M <= BM;
+    if (w_nk && stack)
+        gemm_dma_kernel<false, true, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    else if (w_nk)
         gemm_dma_kernel<false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+    else if (stack)
+        gemm_dma_kernel<false, false, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else
         gemm_dma_kernel<false, false><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     return hipGetLastError();

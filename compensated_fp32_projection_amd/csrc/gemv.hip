@@ -476,6 +476,64 @@ __global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict
     __builtin_nontemporal_store(v, y + m * ldy + n);
 }
 
+// The same merge over four consecutive columns per thread: 16-byte loads of
+// the partial sums (n_pad is a multiple of 4, the partial sums 16-byte
+// aligned), a quarter of the load instructions for the same bytes.  Each
+// column is summed exactly as above (from +0, chunks in order).  VY: rows of
+// y take 16-byte stores (ldy % 4 == 0, y 16-byte aligned).
+constexpr int kMergeBatch4 = 8;
+
+template <bool VY>
+__global__ __launch_bounds__(256) void gemv_merge4_kernel(const float *__restrict__ part, int64_t n_pad,
+                                                          int64_t chunks, int M, int64_t N,
+                                                          float *__restrict__ y, int64_t ldy,
+                                                          const float *__restrict__ bias)
+{
+    const int64_t groups = (N + 3) / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)M * groups) return;
+    const int m = (int)(i / groups);
+    const int64_t n = 4 * (i % groups);
+    const int64_t stride = (int64_t)M * 2 * n_pad;  // from one chunk to the next
+    const float *p = part + (int64_t)m * 2 * n_pad + n;
+    floatx4_t th = {0.0f, 0.0f, 0.0f, 0.0f}, tl = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t c0 = 0; c0 < chunks; c0 += kMergeBatch4) {
+        floatx4_t vh[kMergeBatch4], vl[kMergeBatch4];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch4; ++j) {
+            const bool in = c0 + j < chunks;
+            const floatx4_t *q = reinterpret_cast<const floatx4_t *>(p + (c0 + j) * stride);
+            vh[j] = in ? __builtin_nontemporal_load(q) : floatx4_t{};
+            vl[j] = in ? __builtin_nontemporal_load(reinterpret_cast<const floatx4_t *>(p + (c0 + j) * stride + n_pad))
+                       : floatx4_t{};
+        }
+#pragma unroll
+        for (int j = 0; j < kMergeBatch4; ++j) {
+            if (c0 + j < chunks) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    th[e] += vh[j][e];
+                    tl[e] += vl[j][e];
+                }
+            }
+        }
+    }
+    floatx4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = merge_value(th[e], tl[e]);
+        if (bias && n + e < N) v[e] = v[e] + bias[n + e];
+    }
+    float *out = y + m * ldy + n;
+    if (VY && n + 4 <= N) {
+        __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t *>(out));
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < N) __builtin_nontemporal_store(v[e], out + e);
+    }
+}
+
 // GEGLU merge (the laya.cpp Vulkan guide's fused GEGLU step, graph
 // paragraph): for output (m, n < F), the chunk sums of columns n (gate) and
 // F + n (up) in chunk order, each merged (plus its bias), then
@@ -787,6 +845,17 @@ hipError_t launch_partial_geglu_merge(const float *part, int64_t n_pad, int64_t 
 hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks, int64_t M, int64_t N, float *y,
                                 int64_t ldy, const float *bias, hipStream_t stream)
 {
+    const auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (n_pad % 4 == 0 && al16(part)) {
+        const int64_t threads = M * ((N + 3) / 4);
+        if (M > 0x7FFFFFFF || (threads + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        const dim3 grid((unsigned)((threads + 255) / 256));
+        if (ldy % 4 == 0 && al16(y))
+            gemv_merge4_kernel<true><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+        else
+            gemv_merge4_kernel<false><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+        return hipGetLastError();
+    }
     const int64_t outs = M * N;
     if (M > 0x7FFFFFFF || (outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y,
@@ -834,11 +903,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
         GemvArgs g{x, ldx, w, ldw, part, y, ldy, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), bias, 0};
         hipError_t e = launch_product(g, blocks, stream);
         if (e != hipSuccess || p.chunks == 1) return e;
-        const int64_t outs = M * N;
-        if ((outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks, (int)M,
-                                                                                     N, y, ldy, bias);
-        return hipGetLastError();
+        return launch_partial_merge(part, p.n_pad, p.chunks, M, N, y, ldy, bias, stream);
     }
     if (M > kGemvMaxRows) return hipErrorNotSupported;  // the GEMM path takes it
     switch (M) {

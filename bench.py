@@ -53,7 +53,7 @@ PEAK_HBM_GBS = 8000.0
 K_, N_, M_DEC, M_PRE = 4096, 14336, 1, 8192
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_counters.txt")
 CALIB_BYTES = 512 * 1024 * 1024  # plain device copy of known size, for counter scaling
-GEMM_KERNEL = "gemm_dma_kernel<false, false, false>"  # the plain [K, N] variant
+GEMM_KERNEL = "gemm_dma_kernel<false, false, false, false>"  # the plain [K, N] variant
 COPY_KERNEL_HINT = "copy"
 
 
@@ -147,8 +147,8 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
 
 GEMV_SUMMARY = os.path.join(ROOT, "profiles", "decode_gemv_1x4096x14336_counters.txt")
 GEMV_PRODUCT_KERNEL = "gemv_valu_kernel<1>"  # the M = 1 product dispatch
-GEMV_MERGE_KERNEL = "gemv_merge_kernel"
-GEMV_GRID = 14336                            # threads of the M = 1 merge dispatch
+GEMV_MERGE_KERNEL = "gemv_merge4_kernel"
+GEMV_GRID = 14336 // 4                       # threads of the M = 1 merge dispatch (4 outputs each)
 
 
 def gemv_source_hash() -> str:

@@ -57,12 +57,21 @@ GEMM_KERNEL = "gemm_dma_kernel<false, false, false, false>"  # the plain [K, N] 
 COPY_KERNEL_HINT = "copy"
 
 
-def kernel_source_hash() -> str:
+def _code_hash(names) -> str:
+    """Hash of the code in these csrc files, comments and blank space left
+    out, so that a measured summary stays valid across comment edits."""
     h = hashlib.sha256()
-    for name in ("gemm_dma.hip", "gemm.hip", "tile_order.h", "device_common.h"):
-        with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in names:
+        with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return _code_hash(("gemm_dma.hip", "gemm.hip", "tile_order.h", "device_common.h"))
 
 
 def measured_traffic():
@@ -152,11 +161,7 @@ GEMV_GRID = 14336 // 4                       # threads of the M = 1 merge dispat
 
 
 def gemv_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("gemv.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "compensated_fp32_projection_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    return _code_hash(("gemv.hip", "device_common.h"))
 
 
 def summarize_gemv_counters(fetch_csv, write_csv, out_path, command):

@@ -1,30 +1,36 @@
-// Small-M projection (1 <= M <= 8 rows, decode-sized inputs).
+// Small-M projection (decode-sized inputs: up to 8 rows of x, and up to 16
+// with [K, N] weights that allow 16-byte loads).
 //
 // The laya.cpp Vulkan guide runs small projections at their real batch size,
-// with no padding of the row count.  At M <= 8 the projection streams W once
-// and does little arithmetic per byte, so it is bound by HBM bandwidth; W is
-// read in whole 1 KiB row segments (512 columns), the access pattern that
-// streams fastest, and K is cut into row chunks so that there are enough
-// blocks to keep every CU loading.
+// with no padding of the row count.  With few rows the projection streams W
+// once and does little arithmetic per byte, so it is bound by HBM bandwidth;
+// W is read in whole 1 KiB row segments (512 columns), the access pattern
+// that streams fastest, and K is cut into row chunks so that there are
+// enough blocks to keep every CU loading.
 //
 // Two dispatches, as in the guide's description of the method (the products,
 // then the merge as one dispatch):
 //
-//  1. gemv_mfma_kernel -- split + both products.  A block (4 waves) owns one
-//     512-column tile of one row chunk and walks it in stages of 32 rows
+//  1. gemv_mfma_kernel<G> -- split + both products.  A block (4 waves) owns
+//     one 512-column tile of one row chunk and walks it in stages of 32 rows
 //     through a four-buffer LDS ring filled by LDS-DMA loads (W: one 1 KiB
 //     row per wave instruction, streaming cache policy; x: the chunk's 32
 //     columns of every row, 4 bytes per lane, so x needs no alignment).
-//     The matrix unit does the products: the hi and lo halves of the M rows
-//     are interleaved into the 16 rows of one v_mfma_f32_16x16x32_f16 A
-//     operand (row 2m = hi of x row m, row 2m + 1 = lo), so one MFMA chain
-//     forms C_hi and C_lo together with FP32 accumulators, and the split of
-//     x happens in registers as the A fragment is built.  Each wave owns 128
-//     columns (8 MFMA tiles); no reduction across waves is needed.  The block
-//     writes its chunk's C_hi and C_lo partial sums to the workspace, or, when
-//     K is a single chunk, merges and writes y itself (no second dispatch).
-//  2. gemv_merge_kernel -- for every output, sums the chunk partials of C_hi
-//     and of C_lo in chunk order, then merges y = C_hi + C_lo / 1024.
+//     The matrix unit does the products: the hi and lo halves of each group
+//     of 8 rows are interleaved into the 16 rows of one
+//     v_mfma_f32_16x16x32_f16 A operand (row 2m = hi of x row m, row 2m + 1
+//     = lo), so one MFMA chain forms C_hi and C_lo together with FP32
+//     accumulators, and the split of x happens in registers as the A
+//     fragment is built; G = 2 groups share every B fragment.  Each wave
+//     owns 128 columns (8 MFMA tiles); no reduction across waves is needed.
+//     The block writes its chunk's C_hi and C_lo partial sums to the
+//     workspace, or, when K is a single chunk, merges and writes y itself
+//     (no second dispatch).  For M <= 2, gemv_valu_kernel runs the same
+//     chunks with FP32 FMAs on the vector unit and deeper load queues.
+//  2. gemv_merge4_kernel (gemv_merge_kernel where 16-byte loads of the
+//     partial sums are not possible) -- for every output, sums the chunk
+//     partials of C_hi and of C_lo in chunk order, then merges
+//     y = C_hi + C_lo / 1024.  The split-K GEMM path uses it too.
 //
 // Every summation order is fixed, so results are identical from run to run.
 // W that is not 16-byte aligned with ldw % 8 == 0 (or too large for 32-bit

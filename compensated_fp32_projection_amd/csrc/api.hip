@@ -65,9 +65,12 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace layout, from the caller's pointer rounded up to 256 bytes.
-// M > 8: the hi plane, then the lo plane, each [M, ldh] FP16 with ldh = K
-// rounded up to 8 (16-byte rows), each starting on a 256-byte boundary.
-// M <= 8: the FP32 per-chunk partial sums of the small-M path (GemvPlan).
+// GEMM path (M > 8): the hi plane, then the lo plane, each [M, ldh] FP16
+// with ldh = K rounded up to 8 (16-byte rows), each starting on a 256-byte
+// boundary, then the split-K partial sums when K is split.
+// Small-M path (M <= 8, and M <= 16 with [K, N] weights): the FP32
+// per-chunk partial sums (GemvPlan) from the start.  For 8 < M <= 16 the
+// size covers both, since the small-M dispatch may decline the operands.
 int64_t split_ld(int64_t K) { return (K + 7) / 8 * 8; }
 
 size_t plane_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)split_ld(K) * 2u, kAlign); }

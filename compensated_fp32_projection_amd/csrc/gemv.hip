@@ -924,7 +924,7 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
     }
 }
 
-// GEGLU for 1 <= M <= 8: the product dispatch over all 2F columns of W
+// GEGLU for 1 <= M <= 16: the product dispatch over all 2F columns of W
 // [K, 2F] (partial sums always, even for a single chunk), then the GEGLU
 // merge.  hipErrorNotSupported (nothing enqueued) when W does not allow the
 // buffer path or `part` is missing or too small.

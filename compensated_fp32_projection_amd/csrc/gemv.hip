@@ -670,93 +670,205 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 // ---- W given as [N, K] (a torch.nn.Linear weight: each output column's
 // weights are one K-contiguous row) ----------------------------------------
 //
-// Every output column streams its own row of W, so no column strip problem
-// arises and no partial sums cross blocks: one dispatch.  A block of 16 waves
-// owns 16 columns; per 32-deep k-step, lane l loads 16 bytes of row nb + l %
-// 16 at k = 8 (l / 16) (exactly its MFMA B fragment, no LDS) and the 8
-// matching values of x (two 16-byte loads), splits them and feeds one
-// v_mfma_f32_16x16x32_f16 with the hi and lo rows interleaved as above.  Wave
-// w takes k-steps w, w + 16, ..., so at any time the block's waves read one
-// contiguous 1 KiB run of each of its 16 rows; kNkU k-steps of loads are in
-// flight per wave.  The 16 waves' accumulators are summed in wave order
-// through LDS and the lane that holds both rows of an output merges it (and
-// adds the bias).  Needs K % 8 == 0 (a 16-byte granule is all in or all out),
-// W and x 16-byte aligned with ldw % 8 == 0 and ldx % 4 == 0.
-constexpr int kNkWaves = 16;
-constexpr int kNkU = 4;
-// Cache policy of the W loads: sc0 (bit 0).  Each lane reads half of a
-// 128-byte line and the neighbouring wave the other half; without the
-// streaming hint the line can serve both (measured 29.7 -> 27.1 us at
-// 1 x 4096 x 14336, against the streaming policy the [K, N] kernels use).
-constexpr int kNkAux = 1;
+// Every output column streams its own row of W, so the 1 KiB pieces that
+// stream fastest lie along K and no partial sums cross blocks: one dispatch.
+// A block (8 waves) owns 64 W rows (output columns) over all of K and walks
+// them in stages of 32 KiB through the four-buffer LDS ring: stage s holds
+// rows 32 (s & 1) .. + 31 of the block at k = 512 (s >> 1) .. + 511, one
+// whole 1 KiB piece of each row, each piece one LDS-DMA load (streaming
+// cache policy: every byte of W is read once).  Row r of a stage keeps its
+// granule g at slot 64 r + (g ^ (r % 16)), so the 16 rows an MFMA B fragment
+// reads at one granule fall in 16 different bank groups, and a B fragment is
+// one ds_read_b128.  Wave w multiplies k-steps 2w and 2w + 1 of every piece:
+// its A operands (x split in registers, the hi and lo rows interleaved as
+// above) are loaded one piece ahead and serve both row halves.  At the end
+// the waves' sums are added in wave order through LDS, and the lane that
+// holds both rows of an output merges it (and adds the bias).  Measured at
+// 1..8 x 4096 x 14336 with W streamed from HBM: 23.6-24.6 us, against
+// 27-36 us for 16 waves per 16 columns loading their B fragments straight
+// from memory (64-byte pieces of each row per wave instruction); 4 or 16
+// waves per block, and walking one row half through all of K before the
+// other, were slower.  G = 2 takes 9 to 16 rows of x as two groups of 8,
+// each B fragment feeding both groups' MFMAs.  Needs K % 8 == 0 (a 16-byte
+// granule is all in or all out), W and x 16-byte aligned with ldw % 8 == 0
+// and ldx % 4 == 0.
+constexpr int kNkWaves = 8;
+constexpr int kNkRows = 64;                       // W rows (output columns) per block
+constexpr int kNkPiece = 512;                     // k per row piece (1 KiB)
+constexpr int kNkLoads = 32 / kNkWaves;           // row pieces per wave per stage
+constexpr int kNkSteps = kNkPiece / 32 / kNkWaves;  // k-steps per wave per piece
+constexpr int kNkXLoads = 2 * kNkSteps;           // 16-byte x loads per wave, piece and group
+static_assert(kNkRows / 2 * (kNkPiece / 8) == kWSlots, "a stage fills one ring buffer");
 
+__device__ __forceinline__ int nk_slot(int r, int g) { return r * (kNkPiece / 8) + (g ^ (r & 15)); }
+
+template <int G>
 __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__restrict__ x, int64_t ldx,
                                                                 const uint16_t *__restrict__ w, int64_t ldw,
                                                                 float *__restrict__ y, int64_t ldy,
                                                                 const float *__restrict__ bias, int M, int64_t N,
                                                                 int64_t K)
 {
-    __shared__ floatx4_t red[kNkWaves][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nb = (int64_t)blockIdx.x * 16;
-    const int64_t n = nb + (lane & 15);
-    const int kq = lane >> 4;
-    const int ai = lane & 15;
-    const int am = ai >> 1;
-    const bool a_lo = ai & 1;
+    const int64_t n0 = (int64_t)blockIdx.x * kNkRows;
+    const int pieces = (int)((K + kNkPiece - 1) / kNkPiece);
+    const int nst = 2 * pieces;
 
     const __amdgpu_buffer_rsrc_t rs_w =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(w), 0, (int)(N * ldw * 2), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_x =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), 0, (int)(M * ldx * 4), kBufferWord3);
-    // Granule k = k0 + 8 kq of this lane's W row and x row, while k < K.
-    const int w_base = n < N ? (int)((n * ldw + 8 * kq) * 2) : 0;
-    const int x_base = am < M ? (int)((am * ldx + 8 * kq) * 4) : 0;
-    const int w_kend = n < N ? (int)K - 8 * kq : INT_MIN;
-    const int x_kend = am < M ? (int)K - 8 * kq : INT_MIN;
 
-    floatx4_t acc = floatx4_t{};
-    for (int k0 = 32 * wave; k0 < (int)K; k0 += 32 * kNkWaves * kNkU) {
-        uint4 wv[kNkU];
-        floatx4_t xa[kNkU], xb[kNkU];
+    // DMA sources: the wave loads stage rows kNkLoads wave + j; lane l fills
+    // slot l of the row, i.e. granule l ^ (row % 16) of the piece.
+    int w_base[2][kNkLoads], w_k[kNkLoads];
 #pragma unroll
-        for (int u = 0; u < kNkU; ++u) {
-            const int k = k0 + 32 * kNkWaves * u;
-            const int ox = k < x_kend ? x_base + 4 * k : kNoOffset;
-            xa[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 0, 0));
-            xb[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ox, 16, 0));
-        }
+    for (int j = 0; j < kNkLoads; ++j) {
+        const int r = kNkLoads * wave + j;
+        const int gr = lane ^ (r & 15);
+        w_k[j] = 8 * gr;
 #pragma unroll
-        for (int u = 0; u < kNkU; ++u) {
-            const int k = k0 + 32 * kNkWaves * u;
-            const int ow = k < w_kend ? w_base + 2 * k : kNoOffset;
-            wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, ow, 0, kNkAux));
-        }
-#pragma unroll
-        for (int u = 0; u < kNkU; ++u) {
-            half8_t a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                _Float16 h, l;
-                split_value(e < 4 ? xa[u][e] : xb[u][e - 4], h, l);  // rows past M read 0: (0, 0)
-                a[e] = a_lo ? l : h;
-            }
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, wv[u]), acc, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+            const int64_t n = n0 + 32 * h + r;
+            w_base[h][j] = n < N ? (int)((n * ldw + 8 * gr) * 2) : -1;
         }
     }
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave != 0 || n >= N) return;
-    floatx4_t t = red[0][lane];
-    for (int v = 1; v < kNkWaves; ++v) t += red[v][lane];
-    // 16x16 accumulator: rows 4 kq + e, column lane % 16; rows 2m, 2m + 1 are
-    // hi, lo of x row m.
+    auto issue = [&](auto buf_tag, int s) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf_tag)::value;
+        uint4 *buf = wring<B>();
+        const int p = s >> 1;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int m = 2 * kq + q;
+        for (int j = 0; j < kNkLoads; ++j) {
+            const int base = (s & 1) ? w_base[1][j] : w_base[0][j];
+            const int o = (s < nst && base >= 0 && kNkPiece * p + w_k[j] < (int)K) ? base + 2 * kNkPiece * p
+                                                                                    : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(buf + 64 * (kNkLoads * wave + j)), 16,
+                                                     o, 0, 0, kStreamAux);
+        }
+    };
+
+    // A operand: lane l is row i = l % 16 (x row i / 2; hi for even i, lo
+    // for odd i) at k = 8 (l / 16) .. + 7 of the k-step.
+    const int ai = lane & 15, am = ai >> 1, kq = lane >> 4;
+    const bool a_lo = ai & 1;
+    int x_base[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) x_base[q] = 8 * q + am < M ? (int)(((8 * q + am) * ldx + 8 * kq) * 4) : -1;
+    floatx4_t xs[2][G][kNkSteps][2];  // two pieces of x: the current one and the next
+    auto load_x = [&](auto set_tag, int p) __attribute__((always_inline)) {
+        constexpr int X = decltype(set_tag)::value;
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int t = 0; t < kNkSteps; ++t) {
+                const int k = kNkPiece * p + 32 * (kNkSteps * wave + t);
+                const bool ok = x_base[q] >= 0 && p < pieces && k + 8 * kq < (int)K;
+                xs[X][q][t][0] = __builtin_bit_cast(
+                    floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k : kNoOffset, 0, 0));
+                xs[X][q][t][1] = __builtin_bit_cast(
+                    floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k + 16 : kNoOffset, 0, 0));
+            }
+    };
+    half8_t af[G][kNkSteps];
+    auto build_a = [&](auto set_tag) __attribute__((always_inline)) {
+        constexpr int X = decltype(set_tag)::value;
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int t = 0; t < kNkSteps; ++t)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    _Float16 h, l;
+                    split_value(e < 4 ? xs[X][q][t][0][e] : xs[X][q][t][1][e - 4], h, l);  // rows past M read 0
+                    af[q][t][e] = a_lo ? l : h;
+                }
+    };
+
+    floatx4_t acc[G][4];  // [group][row half][16-column block]
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[q][b] = floatx4_t{};
+
+    // One stage: (even stages) form this piece's A operands and load the next
+    // piece's x; read the B fragments; refill the buffer read one stage ago
+    // with stage s + 3; multiply; then wait until stage s + 1 has landed (and,
+    // before an even stage, the x it needs) and the LDS reads are done.  The
+    // x loads of piece p + 1 go out in stage 2p, before that stage's W loads,
+    // so two stages of W loads and one piece of x may stay in flight there.
+    auto stage = [&](auto buf_tag, int s) __attribute__((always_inline)) {
+        constexpr int S = decltype(buf_tag)::value;
+        const uint4 *buf = wring<S>();
+        if constexpr ((S & 1) == 0) {
+            build_a(std::integral_constant<int, (S >> 1) & 1>{});
+            load_x(std::integral_constant<int, ((S >> 1) + 1) & 1>{}, (s >> 1) + 1);
+        }
+        half8_t bf[kNkSteps][2];
+#pragma unroll
+        for (int t = 0; t < kNkSteps; ++t)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+                bf[t][jb] = __builtin_bit_cast(half8_t, buf[nk_slot(16 * jb + (lane & 15), 4 * (kNkSteps * wave + t) + kq)]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(std::integral_constant<int, (S + 3) & 3>{}, s + 3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < kNkSteps; ++t)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int q = 0; q < G; ++q)
+                    acc[q][2 * (S & 1) + jb] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(af[q][t], bf[t][jb], acc[q][2 * (S & 1) + jb], 0, 0, 0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((S & 1) ? 2 * kNkLoads : 2 * kNkLoads + G * kNkXLoads));
+        __builtin_amdgcn_s_barrier();
+    };
+
+    load_x(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 0>{}, 0);
+    issue(std::integral_constant<int, 1>{}, 1);
+    issue(std::integral_constant<int, 2>{}, 2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kNkLoads));  // x of piece 0 and stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    for (int s = 0; s < nst; s += 4) {  // nst is even
+        stage(std::integral_constant<int, 0>{}, s);
+        stage(std::integral_constant<int, 1>{}, s + 1);
+        if (s + 2 < nst) {
+            stage(std::integral_constant<int, 2>{}, s + 2);
+            stage(std::integral_constant<int, 3>{}, s + 3);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the trailing zero loads, before the ring is reused
+    __builtin_amdgcn_s_barrier();
+
+    // The waves' sums, [wave][block][lane] in ring buffer q for group q,
+    // added in wave order.  16x16 accumulator: rows 4 kq + e, column
+    // lane % 16; rows 2m, 2m + 1 are hi, lo of x row 8 q + m.
+    static_assert(G <= 2 && kNkWaves * 4 * 64 * 16 <= kWSlots * 16, "each group's sums fit one ring buffer");
+    auto red = [&](int q) { return reinterpret_cast<floatx4_t *>(q == 0 ? wring<0>() : wring<1>()); };
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) red(q)[(wave * 4 + b) * 64 + lane] = acc[q][b];
+    __syncthreads();
+    if (threadIdx.x >= G * 4 * 64) return;
+    const int q = threadIdx.x >> 8;
+    const int b = (threadIdx.x >> 6) & 3;
+    const floatx4_t *rq = red(q);
+    floatx4_t t = rq[b * 64 + lane];
+    for (int v = 1; v < kNkWaves; ++v) {
+        const floatx4_t u = rq[(v * 4 + b) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] += u[e];
+    }
+    const int64_t n = n0 + 16 * b + (lane & 15);
+    if (n >= N) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int m = 8 * q + 2 * kq + h;
         if (m >= M) continue;
-        float v = merge_value(t[2 * q], t[2 * q + 1]);
+        float v = merge_value(t[2 * h], t[2 * h + 1]);
         if (bias) v = v + bias[n];
         y[m * ldy + n] = v;
     }
@@ -957,18 +1069,23 @@ hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int
 hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias)
 {
-    if (M < 1 || M > kGemvMaxRows) return hipErrorInvalidValue;
+    if (M < 1 || M > kGemvMaxRowsKN) return hipErrorInvalidValue;
     constexpr int64_t kLimit = kNoOffset - (1 << 20);
     const bool fast = K > 0 && K % 8 == 0 && ldw % 8 == 0 && ldx % 4 == 0 &&
                       ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
                       N * ldw * 2 < kLimit && M * ldx * 4 < kLimit && K < kLimit / 64;
     if (fast) {
-        const int64_t blocks = (N + 15) / 16;
+        const int64_t blocks = (N + kNkRows - 1) / kNkRows;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        gemv_nk_kernel<<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias, (int)M,
-                                                                            N, K);
+        if (M <= kGemvMaxRows)
+            gemv_nk_kernel<1><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
+                                                                                   (int)M, N, K);
+        else
+            gemv_nk_kernel<2><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
+                                                                                   (int)M, N, K);
         return hipGetLastError();
     }
+    if (M > kGemvMaxRows) return hipErrorNotSupported;  // the GEMM path takes it
     switch (M) {
     case 1: return launch_nk_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);
     case 2: return launch_nk_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias);

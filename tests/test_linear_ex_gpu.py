@@ -5,11 +5,11 @@ weights in either layout ([K, N], or [N, K] as torch.nn.Linear stores them).
     (small-M chunked, small-M single chunk, small-M [N, K], the split-inside
     GEMM, split + GEMM, the generic GEMM, K = 0), since the bias is one FP32
     addition after the merge;
-  * [N, K] weights, M > 8: the same tiles, operands and k order as [K, N], so
-    bit-identical to the [K, N] call on the transposed weights;
-  * [N, K] weights, M <= 8: a different kernel (one MFMA chain per output
-    over all of K), checked against the FP64 reference, for determinism and
-    against the single-FP16 product bound;
+  * [N, K] weights, M > 16: the same tiles, operands and k order as [K, N],
+    so bit-identical to the [K, N] call on the transposed weights;
+  * [N, K] weights, M <= 16: a different kernel (each block streams 64 whole
+    W rows through LDS in 1 KiB pieces of K, the waves' sums added in wave
+    order), checked against the FP64 reference and for determinism;
   * [K, N] without a bias is exactly cfp32_linear.
 """
 import numpy as np
@@ -91,12 +91,16 @@ def test_nk_matches_kn_bitwise_above_16_rows(M, K, N):
     assert np.array_equal(y_kn.view(np.uint32), y_nk.view(np.uint32))
 
 
-@pytest.mark.parametrize("M", range(1, 9))
+@pytest.mark.parametrize("M", range(1, 17))
 def test_nk_small_m(M):
-    """M <= 8 with [N, K] weights: ragged N, K % 8 != 0 and unaligned weights
-    (the generic kernel), and the full decode shape (one MFMA chain per
-    output)."""
-    cases = [(4096, 14336, 0, 0), (1000, 777, 0, 0), (1001, 64, 0, 0), (64, 33, 1, 0), (8, 1, 0, 3), (96, 520, 0, 5)]
+    """M <= 16 with [N, K] weights.  The LDS-DMA kernel (64 W rows per block,
+    1 KiB pieces of K; one or two groups of 8 rows of x): the full decode
+    shape, K below one piece, exactly one piece, a ragged last piece, an odd
+    number of pieces with a padded row stride, 16 pieces, and N with a
+    partial last block (down to one row).  K % 8 != 0 and unaligned weights
+    take the generic kernel (M <= 8) or the GEMM path."""
+    cases = [(4096, 14336, 0, 0), (1000, 777, 0, 0), (256, 100, 0, 0), (512, 65, 0, 0), (1536, 130, 0, 8),
+             (8192, 200, 0, 0), (1001, 64, 0, 0), (64, 33, 1, 0), (8, 1, 0, 3), (96, 520, 0, 5)]
     for K, N, w_off, w_pad in cases:
         A, W = workloads.random_case(M * 100 + K + N, M, K, N, a_scale=30.0)
         note(f"linear_ex nk small M={M} K={K} N={N} w_off={w_off} w_pad={w_pad}")

@@ -64,19 +64,22 @@ SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
 def test_split_k_against_reference_and_across_kernels(M, K, N):
-    """Unaligned weights (generic kernel) in both layouts, and aligned ones
-    (LDS-DMA kernel with the hi and lo rows stacked into one tile; [K, N]
-    from 17 rows up, below that the small-M dispatches take it), cut K at
-    the same places: the same bits, within tolerance."""
+    """Unaligned weights (generic kernel) in both layouts, and from 17 rows
+    up aligned ones (LDS-DMA kernel with the hi and lo rows stacked into one
+    tile), cut K at the same places: the same bits, within tolerance.  Up to
+    16 rows aligned weights take the small-M dispatches (checked against the
+    reference)."""
     need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
     assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
     A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
     note(f"split-K {M}x{K}x{N}")
     y = run(A, W, w_offset=1)
     check(y, A, W, f"split-K {M}x{K}x{N}")
-    runs = [run(A, W, layout=cf.W_NK, w_offset=1), run(A, W, layout=cf.W_NK)]
+    runs = [run(A, W, layout=cf.W_NK, w_offset=1)]
     if M > 16:
-        runs.append(run(A, W))
+        runs += [run(A, W), run(A, W, layout=cf.W_NK)]
+    else:  # aligned [N, K] weights up to 16 rows take the small-M [N, K] dispatch
+        check(run(A, W, layout=cf.W_NK), A, W, f"small-M [N, K] {M}x{K}x{N}")
     for y2 in runs:
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
     y3 = run(A, W, w_offset=1)

@@ -211,9 +211,9 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
                                            bias));
     }
 
-    if (nk && M <= cfp32::kGemvMaxRowsKN && K > 0) {
-        // Up to 16 rows of x with [N, K] weights: the small-M [N, K] dispatch
-        // with two groups of 8 rows; it enqueues nothing and returns
+    if (nk && M <= cfp32::kGemvMaxRowsNK && K > 0) {
+        // Up to 32 rows of x with [N, K] weights: the small-M [N, K] dispatch
+        // with two or four groups of 8 rows; it enqueues nothing and returns
         // hipErrorNotSupported when W or x do not allow 16-byte loads, and the
         // GEMM path below runs instead.
         const hipError_t e = cfp32::launch_gemv_nk(x, ldx, w, ldw, y, ldy, M, N, K, s, bias);

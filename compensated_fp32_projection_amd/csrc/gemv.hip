@@ -688,8 +688,8 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 // 27-36 us for 16 waves per 16 columns loading their B fragments straight
 // from memory (64-byte pieces of each row per wave instruction); 4 or 16
 // waves per block, and walking one row half through all of K before the
-// other, were slower.  G = 2 takes 9 to 16 rows of x as two groups of 8,
-// each B fragment feeding both groups' MFMAs.  Needs K % 8 == 0 (a 16-byte
+// other, were slower.  G = 2 and 4 take up to 16 and 32 rows of x as groups
+// of 8, each B fragment feeding every group's MFMAs.  Needs K % 8 == 0 (a 16-byte
 // granule is all in or all out), W and x 16-byte aligned with ldw % 8 == 0
 // and ldx % 4 == 0.
 constexpr int kNkWaves = 8;
@@ -755,24 +755,24 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     int x_base[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) x_base[q] = 8 * q + am < M ? (int)(((8 * q + am) * ldx + 8 * kq) * 4) : -1;
-    floatx4_t xs[2][G][kNkSteps][2];  // two pieces of x: the current one and the next
-    auto load_x = [&](auto set_tag, int p) __attribute__((always_inline)) {
-        constexpr int X = decltype(set_tag)::value;
+    // x of one piece: read into the A operands at the start of an even
+    // stage, then overwritten by the next piece's loads.
+    floatx4_t xs[G][kNkSteps][2];
+    auto load_x = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < G; ++q)
 #pragma unroll
             for (int t = 0; t < kNkSteps; ++t) {
                 const int k = kNkPiece * p + 32 * (kNkSteps * wave + t);
                 const bool ok = x_base[q] >= 0 && p < pieces && k + 8 * kq < (int)K;
-                xs[X][q][t][0] = __builtin_bit_cast(
+                xs[q][t][0] = __builtin_bit_cast(
                     floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k : kNoOffset, 0, 0));
-                xs[X][q][t][1] = __builtin_bit_cast(
+                xs[q][t][1] = __builtin_bit_cast(
                     floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k + 16 : kNoOffset, 0, 0));
             }
     };
     half8_t af[G][kNkSteps];
-    auto build_a = [&](auto set_tag) __attribute__((always_inline)) {
-        constexpr int X = decltype(set_tag)::value;
+    auto build_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < G; ++q)
 #pragma unroll
@@ -780,7 +780,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     _Float16 h, l;
-                    split_value(e < 4 ? xs[X][q][t][0][e] : xs[X][q][t][1][e - 4], h, l);  // rows past M read 0
+                    split_value(e < 4 ? xs[q][t][0][e] : xs[q][t][1][e - 4], h, l);  // rows past M read 0
                     af[q][t][e] = a_lo ? l : h;
                 }
     };
@@ -801,8 +801,8 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
         constexpr int S = decltype(buf_tag)::value;
         const uint4 *buf = wring<S>();
         if constexpr ((S & 1) == 0) {
-            build_a(std::integral_constant<int, (S >> 1) & 1>{});
-            load_x(std::integral_constant<int, ((S >> 1) + 1) & 1>{}, (s >> 1) + 1);
+            build_a();
+            load_x((s >> 1) + 1);
         }
         half8_t bf[kNkSteps][2];
 #pragma unroll
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
         __builtin_amdgcn_s_barrier();
     };
 
-    load_x(std::integral_constant<int, 0>{}, 0);
+    load_x(0);
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, 1);
     issue(std::integral_constant<int, 2>{}, 2);
@@ -845,32 +845,34 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     // The waves' sums, [wave][block][lane] in ring buffer q for group q,
     // added in wave order.  16x16 accumulator: rows 4 kq + e, column
     // lane % 16; rows 2m, 2m + 1 are hi, lo of x row 8 q + m.
-    static_assert(G <= 2 && kNkWaves * 4 * 64 * 16 <= kWSlots * 16, "each group's sums fit one ring buffer");
-    auto red = [&](int q) { return reinterpret_cast<floatx4_t *>(q == 0 ? wring<0>() : wring<1>()); };
+    static_assert(G <= 4 && kNkWaves * 4 * 64 * 16 <= kWSlots * 16, "each group's sums fit one ring buffer");
+    auto red = [&](int q) {
+        return reinterpret_cast<floatx4_t *>(q == 0 ? wring<0>() : q == 1 ? wring<1>() : q == 2 ? wring<2>() : wring<3>());
+    };
 #pragma unroll
     for (int q = 0; q < G; ++q)
 #pragma unroll
         for (int b = 0; b < 4; ++b) red(q)[(wave * 4 + b) * 64 + lane] = acc[q][b];
     __syncthreads();
-    if (threadIdx.x >= G * 4 * 64) return;
-    const int q = threadIdx.x >> 8;
     const int b = (threadIdx.x >> 6) & 3;
-    const floatx4_t *rq = red(q);
-    floatx4_t t = rq[b * 64 + lane];
-    for (int v = 1; v < kNkWaves; ++v) {
-        const floatx4_t u = rq[(v * 4 + b) * 64 + lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] += u[e];
-    }
     const int64_t n = n0 + 16 * b + (lane & 15);
-    if (n >= N) return;
+    for (int q = threadIdx.x >> 8; q < G; q += 64 * kNkWaves / 256) {
+        const floatx4_t *rq = red(q);
+        floatx4_t t = rq[b * 64 + lane];
+        for (int v = 1; v < kNkWaves; ++v) {
+            const floatx4_t u = rq[(v * 4 + b) * 64 + lane];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int m = 8 * q + 2 * kq + h;
-        if (m >= M) continue;
-        float v = merge_value(t[2 * h], t[2 * h + 1]);
-        if (bias) v = v + bias[n];
-        y[m * ldy + n] = v;
+            for (int e = 0; e < 4; ++e) t[e] += u[e];
+        }
+        if (n >= N) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = 8 * q + 2 * kq + h;
+            if (m >= M) continue;
+            float v = merge_value(t[2 * h], t[2 * h + 1]);
+            if (bias) v = v + bias[n];
+            y[m * ldy + n] = v;
+        }
     }
 }
 
@@ -1069,7 +1071,7 @@ hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int
 hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias)
 {
-    if (M < 1 || M > kGemvMaxRowsKN) return hipErrorInvalidValue;
+    if (M < 1 || M > kGemvMaxRowsNK) return hipErrorInvalidValue;
     constexpr int64_t kLimit = kNoOffset - (1 << 20);
     const bool fast = K > 0 && K % 8 == 0 && ldw % 8 == 0 && ldx % 4 == 0 &&
                       ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
@@ -1080,8 +1082,11 @@ hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_
         if (M <= kGemvMaxRows)
             gemv_nk_kernel<1><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
                                                                                    (int)M, N, K);
-        else
+        else if (M <= 2 * kGemvMaxRows)
             gemv_nk_kernel<2><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
+                                                                                   (int)M, N, K);
+        else
+            gemv_nk_kernel<4><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
                                                                                    (int)M, N, K);
         return hipGetLastError();
     }

@@ -108,9 +108,11 @@ constexpr int64_t kGemvMaxRows = 8;
 // weights at M x 4096 x 14336: M = 9 / 16 take 25.7 / 28.0 us against
 // 35 / 36 us for split K, while four groups, M = 32, took 42 us against 40).
 constexpr int64_t kGemvMaxRowsKN = 16;
+// [N, K] weights: up to 32 rows (four groups of 8).
+constexpr int64_t kGemvMaxRowsNK = 32;
 
 // Small-M path for W given as [N, K] (ldw >= K): one dispatch, no workspace.
-// M <= 8 always; 8 < M <= 16 only with 16-byte loads of W and x, else
+// M <= 8 always; 8 < M <= 32 only with 16-byte loads of W and x, else
 // hipErrorNotSupported with nothing enqueued (the GEMM path takes it).
 hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias = nullptr);

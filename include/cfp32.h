@@ -201,11 +201,11 @@ CFP32_API size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K
  *              cfp32_linear_ex_workspace_bytes(M, N, K, w_layout).
  * With CFP32_W_KN and no bias this is exactly cfp32_linear (same kernels,
  * same bits); without the bias, y equals the bias-free call to the bit.
- * CFP32_W_NK, M <= 16: one dispatch with no workspace, each block
- * streaming 64 whole W rows through LDS (M <= 8 always; 8 < M <= 16 when
+ * CFP32_W_NK, M <= 32: one dispatch with no workspace, each block
+ * streaming 64 whole W rows through LDS (M <= 8 always; 8 < M <= 32 when
  * K % 8 == 0, ldw % 8 == 0, ldx % 4 == 0 and w, x are 16-byte aligned,
- * else the GEMM path).  CFP32_W_NK, M > 16: the GEMM paths; for M > 16
- * both layouts give the same bits.
+ * else the GEMM path).  CFP32_W_NK, M > 32: the GEMM paths, with the same
+ * bits as CFP32_W_KN.
  * Unknown layouts give CFP32_ERR_INVALID_VALUE. */
 CFP32_API cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int w_layout,
                              const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,

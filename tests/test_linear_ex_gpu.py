@@ -5,9 +5,9 @@ weights in either layout ([K, N], or [N, K] as torch.nn.Linear stores them).
     (small-M chunked, small-M single chunk, small-M [N, K], the split-inside
     GEMM, split + GEMM, the generic GEMM, K = 0), since the bias is one FP32
     addition after the merge;
-  * [N, K] weights, M > 16: the same tiles, operands and k order as [K, N],
+  * [N, K] weights, M > 32: the same tiles, operands and k order as [K, N],
     so bit-identical to the [K, N] call on the transposed weights;
-  * [N, K] weights, M <= 16: a different kernel (each block streams 64 whole
+  * [N, K] weights, M <= 32: a different kernel (each block streams 64 whole
     W rows through LDS in 1 KiB pieces of K, the waves' sums added in wave
     order), checked against the FP64 reference and for determinism;
   * [K, N] without a bias is exactly cfp32_linear.
@@ -82,8 +82,8 @@ def test_bias_with_k_zero():
 
 @pytest.mark.parametrize("M,K,N", [(40, 256, 300), (8192, 512, 512), (2048, 1024, 4608), (300, 1000, 777),
                                    (4100, 64, 8200)])
-def test_nk_matches_kn_bitwise_above_16_rows(M, K, N):
-    """M > 16: [N, K] weights reach the same tiles with the same k order."""
+def test_nk_matches_kn_bitwise_above_32_rows(M, K, N):
+    """M > 32: [N, K] weights reach the same tiles with the same k order."""
     A, W = workloads.random_case(M * 5 + K + N, M, K, N, a_scale=10.0)
     note(f"linear_ex nk vs kn {M}x{K}x{N}")
     y_kn = run_ex(A, W, cf.W_KN)
@@ -91,10 +91,10 @@ def test_nk_matches_kn_bitwise_above_16_rows(M, K, N):
     assert np.array_equal(y_kn.view(np.uint32), y_nk.view(np.uint32))
 
 
-@pytest.mark.parametrize("M", range(1, 17))
+@pytest.mark.parametrize("M", list(range(1, 18)) + [23, 24, 25, 31, 32])
 def test_nk_small_m(M):
-    """M <= 16 with [N, K] weights.  The LDS-DMA kernel (64 W rows per block,
-    1 KiB pieces of K; one or two groups of 8 rows of x): the full decode
+    """M <= 32 with [N, K] weights.  The LDS-DMA kernel (64 W rows per block,
+    1 KiB pieces of K; one, two or four groups of 8 rows of x): the full decode
     shape, K below one piece, exactly one piece, a ragged last piece, an odd
     number of pieces with a padded row stride, 16 pieces, and N with a
     partial last block (down to one row).  K % 8 != 0 and unaligned weights

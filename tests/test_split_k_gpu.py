@@ -64,11 +64,11 @@ SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
 def test_split_k_against_reference_and_across_kernels(M, K, N):
-    """Unaligned weights (generic kernel) in both layouts, and from 17 rows
-    up aligned ones (LDS-DMA kernel with the hi and lo rows stacked into one
-    tile), cut K at the same places: the same bits, within tolerance.  Up to
-    16 rows aligned weights take the small-M dispatches (checked against the
-    reference)."""
+    """Unaligned weights (generic kernel) in both layouts, and aligned ones
+    from 17 ([K, N]) or 33 ([N, K]) rows up (LDS-DMA kernel with the hi and
+    lo rows stacked into one tile), cut K at the same places: the same bits,
+    within tolerance.  Below that aligned weights take the small-M
+    dispatches (checked against the reference)."""
     need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
     assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
     A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
@@ -77,8 +77,10 @@ def test_split_k_against_reference_and_across_kernels(M, K, N):
     check(y, A, W, f"split-K {M}x{K}x{N}")
     runs = [run(A, W, layout=cf.W_NK, w_offset=1)]
     if M > 16:
-        runs += [run(A, W), run(A, W, layout=cf.W_NK)]
-    else:  # aligned [N, K] weights up to 16 rows take the small-M [N, K] dispatch
+        runs.append(run(A, W))
+    if M > 32:
+        runs.append(run(A, W, layout=cf.W_NK))
+    else:  # aligned [N, K] weights up to 32 rows take the small-M [N, K] dispatch
         check(run(A, W, layout=cf.W_NK), A, W, f"small-M [N, K] {M}x{K}x{N}")
     for y2 in runs:
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))

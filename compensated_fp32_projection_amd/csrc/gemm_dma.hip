@@ -46,6 +46,12 @@
 //   * Loads outside the matrices get an offset no buffer reaches and read as
 //     zero, so partial tiles need no branches; stages past the end are loaded
 //     the same way, which keeps every wait count constant.
+//   * W given as [N, K] (a torch.nn.Linear weight) sits in LDS like A, as
+//     k-granules of each column, and a B fragment is one ds_read_b128.  Its
+//     W ring holds three 64-deep stages (whole 128-byte lines of every W
+//     row; 32-deep stages fetch 64-byte halves) beside a ring of four
+//     32-deep A stages, 160 KiB in all; the k order, and so every bit of the
+//     result, is the [K, N] kernel's.
 #include <type_traits>
 
 #include "device_common.h"
@@ -88,6 +94,37 @@ __shared__ uint4 g_stage3[STAGE_SLOTS];
 // the same layout as the A planes of a ring stage).
 __shared__ uint4 g_conv0[2 * A_SLOTS];
 __shared__ uint4 g_conv1[2 * A_SLOTS];
+
+// W64 variant ([N, K] W): an A ring of four 32-deep stages (both planes,
+// 16 KiB each) and a W ring of three 64-deep stages (256 columns x 8
+// k-granules, 32 KiB each: whole 128-byte lines of every W row).
+constexpr int W64_KG = 8;
+constexpr int W64_SLOTS = BN * W64_KG;
+__shared__ uint4 g_a64_0[2 * A_SLOTS];
+__shared__ uint4 g_a64_1[2 * A_SLOTS];
+__shared__ uint4 g_a64_2[2 * A_SLOTS];
+__shared__ uint4 g_a64_3[2 * A_SLOTS];
+__shared__ uint4 g_w64_0[W64_SLOTS];
+__shared__ uint4 g_w64_1[W64_SLOTS];
+__shared__ uint4 g_w64_2[W64_SLOTS];
+template <int S>
+__device__ __forceinline__ uint4 *a64_buf()
+{
+    if constexpr (S == 0) return g_a64_0;
+    else if constexpr (S == 1) return g_a64_1;
+    else if constexpr (S == 2) return g_a64_2;
+    else return g_a64_3;
+}
+template <int T>
+__device__ __forceinline__ uint4 *w64_buf()
+{
+    if constexpr (T == 0) return g_w64_0;
+    else if constexpr (T == 1) return g_w64_1;
+    else return g_w64_2;
+}
+// Column n's k-granule g: 16 consecutive columns of one granule fall in 16
+// different 16-byte bank groups (columns are 128 bytes apart).
+__device__ __forceinline__ int w64_slot(int n, int g) { return n * W64_KG + (g ^ ((n >> 1) & 7)); }
 
 template <int P>
 __device__ __forceinline__ uint4 *conv_buf()
@@ -193,9 +230,10 @@ __device__ __forceinline__ int a32_slot(int row, int g) { return row * 8 + (g ^ 
 // products over mostly empty rows.  Every accumulator sums the same
 // products in the same k order as in the two-product form, so the partial
 // sums are the same bits; wave row 0 writes them as C_hi, wave row 1 as C_lo.
-template <bool SPLIT, bool WNK, bool GEGLU = false, bool STACK = false>
+template <bool SPLIT, bool WNK, bool GEGLU = false, bool STACK = false, bool W64 = false>
 __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
 {
+    static_assert(!W64 || (WNK && !SPLIT && !GEGLU && !STACK), "W64: plain [N, K] variant");
     static_assert(!STACK || (!SPLIT && !GEGLU && WTM == 64 && BM == 2 * WTM), "STACK: two wave rows, hi then lo");
     constexpr int LPW = STACK ? LOADS_PER_WAVE - 1 : LOADS_PER_WAVE;  // STACK: one A load per wave
     const int tid = threadIdx.x;
@@ -297,6 +335,39 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
             w_kend[jj] = ok ? (int)(kw_stop - k) : 0;
         }
     }
+
+    // W64: the wave's four 1 KiB loads of a 64-deep W stage: load q covers
+    // columns 8 (4 wave + q) .. + 7, lane l column + l / 8 and the granule
+    // that belongs at slot l % 8 of that column.
+    int w64_off[4], w64_kend[4];
+    if constexpr (W64) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 8 * (4 * wave + q) + (lane >> 3);
+            const int gr = (lane & 7) ^ ((c >> 1) & 7);
+            const bool ok = n0 + c < g.N;
+            w64_off[q] = ok ? (int)(((n0 + c) * g.ldw + 8 * gr) * 2) : kNoOffset;
+            w64_kend[q] = ok ? (int)(kw_stop - 8 * gr) : 0;
+        }
+    }
+    auto issue_a64 = [&](auto buf_tag, int64_t k0_64) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf_tag)::value;
+        uint4 *s = a64_buf<B>();
+        const int k0 = (int)k0_64;
+        const int a = k0 < a_kend[0] ? a_off[0] + 2 * k0 : kNoOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_hi, (CFP32_LDS void *)(s + 64 * wave), 16, a, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_lo, (CFP32_LDS void *)(s + A_SLOTS + 64 * wave), 16, a, 0, 0, 0);
+    };
+    auto issue_w64 = [&](auto buf_tag, int64_t k0_64) __attribute__((always_inline)) {
+        constexpr int T = decltype(buf_tag)::value;
+        uint4 *s = w64_buf<T>();
+        const int k0 = (int)k0_64;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int o = k0 < w64_kend[q] ? w64_off[q] + 2 * k0 : kNoOffset;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(s + 64 * (4 * wave + q)), 16, o, 0, 0, 0);
+        }
+    };
 
     auto issue = [&](auto stage_tag, int64_t k0_64) {
         constexpr int S = decltype(stage_tag)::value;
@@ -443,6 +514,70 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         block_barrier();
     };
 
+    if constexpr (W64) {
+        // Stage S of a 12-stage round (relative stage index r, r % 12 == S):
+        // A from buffer S % 4, W from buffer (S / 2) % 3 at k-granules
+        // 4 (S % 2) ..; the memory phase refills A buffer (S + 3) % 4 with
+        // stage r + 3 and, at even S, W buffer (S / 2 + 2) % 3 with the W
+        // stage that starts at r + 4.  Even stages issue 6 loads, odd ones
+        // 2, so at the end of any stage the wait for "all but the newest 8"
+        // covers the A stage r + 1 and the W stage it needs.
+        auto stage64 = [&](auto stage_tag, int64_t s) __attribute__((always_inline)) {
+            constexpr int S = decltype(stage_tag)::value;
+            const uint4 *abuf = a64_buf<S & 3>();
+            const uint4 *wbuf = w64_buf<(S >> 1) % 3>();
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                f0.bw[j] = __builtin_bit_cast(half8_t, wbuf[w64_slot(b_col0 + 16 * j, 4 * (S & 1) + a_kg)]);
+            __builtin_amdgcn_sched_barrier(0);
+            read_a(abuf, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_a64(std::integral_constant<int, (S + 3) & 3>{}, (s + 3) * BK);
+            if constexpr ((S & 1) == 0) issue_w64(std::integral_constant<int, ((S >> 1) + 2) % 3>{}, (s + 4) * BK);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));
+            block_barrier();
+            __builtin_amdgcn_s_setprio(1);
+            mfmas(f0);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+            block_barrier();
+        };
+        issue_w64(std::integral_constant<int, 0>{}, s_begin * BK);
+        issue_a64(std::integral_constant<int, 0>{}, s_begin * BK);
+        issue_w64(std::integral_constant<int, 1>{}, (s_begin + 2) * BK);
+        issue_a64(std::integral_constant<int, 1>{}, (s_begin + 1) * BK);
+        issue_a64(std::integral_constant<int, 2>{}, (s_begin + 2) * BK);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));  // W stage 0 and A stage 0 landed for this wave
+        block_barrier();
+        if (group == 1) block_barrier();
+        const int64_t nkr = nk / 12 * 12;
+        for (int64_t s0 = 0; s0 < nkr; s0 += 12) {
+            stage64(std::integral_constant<int, 0>{}, s_begin + s0);
+            stage64(std::integral_constant<int, 1>{}, s_begin + s0 + 1);
+            stage64(std::integral_constant<int, 2>{}, s_begin + s0 + 2);
+            stage64(std::integral_constant<int, 3>{}, s_begin + s0 + 3);
+            stage64(std::integral_constant<int, 4>{}, s_begin + s0 + 4);
+            stage64(std::integral_constant<int, 5>{}, s_begin + s0 + 5);
+            stage64(std::integral_constant<int, 6>{}, s_begin + s0 + 6);
+            stage64(std::integral_constant<int, 7>{}, s_begin + s0 + 7);
+            stage64(std::integral_constant<int, 8>{}, s_begin + s0 + 8);
+            stage64(std::integral_constant<int, 9>{}, s_begin + s0 + 9);
+            stage64(std::integral_constant<int, 10>{}, s_begin + s0 + 10);
+            stage64(std::integral_constant<int, 11>{}, s_begin + s0 + 11);
+        }
+        if (nkr < nk) stage64(std::integral_constant<int, 0>{}, s_begin + nkr);
+        if (nkr + 1 < nk) stage64(std::integral_constant<int, 1>{}, s_begin + nkr + 1);
+        if (nkr + 2 < nk) stage64(std::integral_constant<int, 2>{}, s_begin + nkr + 2);
+        if (nkr + 3 < nk) stage64(std::integral_constant<int, 3>{}, s_begin + nkr + 3);
+        if (nkr + 4 < nk) stage64(std::integral_constant<int, 4>{}, s_begin + nkr + 4);
+        if (nkr + 5 < nk) stage64(std::integral_constant<int, 5>{}, s_begin + nkr + 5);
+        if (nkr + 6 < nk) stage64(std::integral_constant<int, 6>{}, s_begin + nkr + 6);
+        if (nkr + 7 < nk) stage64(std::integral_constant<int, 7>{}, s_begin + nkr + 7);
+        if (nkr + 8 < nk) stage64(std::integral_constant<int, 8>{}, s_begin + nkr + 8);
+        if (nkr + 9 < nk) stage64(std::integral_constant<int, 9>{}, s_begin + nkr + 9);
+        if (nkr + 10 < nk) stage64(std::integral_constant<int, 10>{}, s_begin + nkr + 10);
+    } else {
     issue(std::integral_constant<int, 0>{}, s_begin * BK);
     issue(std::integral_constant<int, 1>{}, (s_begin + 1) * BK);
     issue(std::integral_constant<int, 2>{}, (s_begin + 2) * BK);
@@ -465,6 +600,7 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
     if (nk4 < nk) stage(std::integral_constant<int, 0>{}, s_begin + nk4);
     if (nk4 + 1 < nk) stage(std::integral_constant<int, 1>{}, s_begin + nk4 + 1);
     if (nk4 + 2 < nk) stage(std::integral_constant<int, 2>{}, s_begin + nk4 + 2);
+    }
     if (group == 0) block_barrier();  // both groups pass the same number of barriers
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // drain the trailing zero loads before the block exits
 
@@ -549,7 +685,7 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool w_fits(int64_t ldw, int64_t N, int64_t K, bool w_nk)
 {
     constexpr int64_t kLim = kNoOffset - (1 << 20);
-    return w_nk ? (N + BN) * ldw * 2 + (int64_t)BK * 2 < kLim : (K + BK) * ldw * 2 + (int64_t)BN * 2 < kLim;
+    return w_nk ? (N + BN) * ldw * 2 + (int64_t)BK * 8 < kLim : (K + BK) * ldw * 2 + (int64_t)BN * 2 < kLim;
 }
 
 }  // namespace
@@ -577,10 +713,13 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
     // Split K over at most 64 rows: the hi and lo rows stacked into one tile
     // (8 x 4096 x 14336 .. 64 x 4096 x 14336: half the matrix-unit work).
     const bool stack = kchunks > 1 && 2 * M <= BM;
+    // [N, K] W (unless stacked): 64-deep W stages, whole 128-byte lines of
+    // every W row per stage (8192 x 4096 x 14336: 1490 -> 1405 us against
+    // 32-deep stages, bit-identical; the [K, N] kernel takes 1415 us).
     if (w_nk && stack)
         gemm_dma_kernel<false, true, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else if (w_nk)
-        gemm_dma_kernel<false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
+        gemm_dma_kernel<false, true, false, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else if (stack)
         gemm_dma_kernel<false, false, false, true><<<dim3((unsigned)blocks), kT, 0, stream>>>(g);
     else

@@ -20,8 +20,9 @@ roofline is taken for the GEMM, the dominant kernel.
 
 One JSON line is printed.  Extra keys: ``breakdown`` (per kernel),
 ``headline`` (the 4096^3 GEMM, the M = 1 decode path in both weight
-layouts and captured in a graph, and batched decode at M = 16 and 64,
-each measured on its own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
+layouts and captured in a graph, batched decode at M = 16 and 64, and the
+FFN projection with [N, K] weights next to the [K, N] split + GEMM, each
+measured on its own), ``fp32_ab_4096`` (the whole compensated projection at 4096^3 next to
 the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
 ``geglu_ffn_8192x4096x7168`` (the FFN projection with its GEGLU fused,
 next to the plain projection of the same operands),
@@ -53,7 +54,7 @@ PEAK_HBM_GBS = 8000.0
 K_, N_, M_DEC, M_PRE = 4096, 14336, 1, 8192
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_prefill_8192x4096x14336_counters.txt")
 CALIB_BYTES = 512 * 1024 * 1024  # plain device copy of known size, for counter scaling
-GEMM_KERNEL = "gemm_dma_kernel<false, false, false, false>"  # the plain [K, N] variant
+GEMM_KERNEL = "gemm_dma_kernel<false, false, false, false, false>"  # the plain [K, N] variant
 COPY_KERNEL_HINT = "copy"
 
 
@@ -478,7 +479,14 @@ def main():
     gemv_nk_us = timed(lambda i: check(cf.cfp32_linear_ex(x1.data_ptr(), K_, Wts[i % 4].data_ptr(), K_, cf.W_NK,
                                                           None, y1.data_ptr(), N_, M_DEC, N_, K_, None, 0, sh),
                                        "decode nk"), 100)
-    del Wts
+    # The FFN projection with those weights: the split, then the [N, K] GEMM
+    # (64-deep W stages), against split_us + gemm_us of the [K, N] step.
+    nk_ws_bytes = cf.cfp32_linear_ex_workspace_bytes(M_PRE, N_, K_, cf.W_NK)
+    nk_ws = torch.empty(max(nk_ws_bytes, 1), dtype=torch.uint8, device=dev)
+    linear_nk_us = timed(lambda i: check(cf.cfp32_linear_ex(x2.data_ptr(), K_, Wts[i % 4].data_ptr(), K_, cf.W_NK,
+                                                            None, y2.data_ptr(), N_, M_PRE, N_, K_,
+                                                            nk_ws.data_ptr(), nk_ws_bytes, sh), "prefill nk"), 20)
+    del Wts, nk_ws
     gemv_us = timed(lambda i: check(cf.cfp32_linear(x1.data_ptr(), K_, Ws[i % 4].data_ptr(), N_, y1.data_ptr(), N_,
                                                     M_DEC, N_, K_, dec_ws.data_ptr(), dec_ws_bytes, sh), "decode"), 100)
     # Batched decode (the rows of the prefill input, same W copies): 16 rows
@@ -589,6 +597,8 @@ def main():
             "gemv_graph_frac_hbm": round(dec_bytes / (gemv_graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "gemv_nk_1x4096x14336_us": round(gemv_nk_us, 2),
             "gemv_nk_frac_hbm": round(dec_bytes / (gemv_nk_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "linear_nk_8192x4096x14336_us": round(linear_nk_us, 2),
+            "linear_kn_8192x4096x14336_us": round(split_us + gemm_us, 2),
             **batched,
         },
         "fp32_ab_4096": {

@@ -452,18 +452,19 @@ __global__ __launch_bounds__(kT) void gemm_dma_kernel(DmaArgs g)
         __builtin_amdgcn_sched_barrier(0);
         read_a(sa, f);
     };
+    // The hi and lo MFMAs of one block back to back, sharing their B
+    // fragment (8192 x 4096 x 14336: about 1% faster than all four hi
+    // blocks of a row before its lo blocks; same bits, each accumulator's k
+    // order is unchanged).
     auto mfmas = [&](const Frags &f) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j) {
                 acc_hi[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.ah[i], f.bw[j], acc_hi[i][j], 0, 0, 0);
-            if constexpr (!STACK) {
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
+                if constexpr (!STACK)
                     acc_lo[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.al[i], f.bw[j], acc_lo[i][j], 0, 0, 0);
             }
-        }
     };
 
     // SPLIT: lane's conversion unit: row 64*group + u/4, k-granule u%4.

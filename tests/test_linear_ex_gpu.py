@@ -91,6 +91,35 @@ def test_nk_matches_kn_bitwise_above_32_rows(M, K, N):
     assert np.array_equal(y_kn.view(np.uint32), y_nk.view(np.uint32))
 
 
+def test_nk_ffn_prefill_full_size_matches_kn():
+    """The FFN projection 8192 x 4096 x 14336 with the weights in both
+    layouts (the [N, K] GEMM with 64-deep W stages, as bench.py times it):
+    the same bits everywhere, and the FP64 reference at sampled rows."""
+    wl = workloads.decode_ffn_pair()
+    A, W = wl.A[1], wl.W
+    M, K = A.shape
+    N = W.shape[1]
+    note("linear_ex nk vs kn 8192x4096x14336")
+    dx = to_dev(A)
+    dw_kn = to_dev(W.view(np.uint16))
+    dw_nk = dw_kn.view(K, N).t().contiguous()
+    outs = []
+    for layout, dw, ldw in ((cf.W_KN, dw_kn, N), (cf.W_NK, dw_nk, K)):
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, layout)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        st = cf.cfp32_linear_ex(dx.data_ptr(), K, dw.data_ptr(), ldw, layout, None, y.data_ptr(), N, M, N, K,
+                                ws.data_ptr(), need, stream_handle())
+        assert st == cf.OK, cf.cfp32_status_string(st)
+        torch.cuda.synchronize()
+        outs.append(y)
+        del ws
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32)), "[N, K] and [K, N] differ"
+    rows = np.random.default_rng(11).choice(M, 48, replace=False)
+    y64, abs64 = oracle.y64(A[rows], W)
+    assert_within_tolerance(to_host(outs[1][torch.from_numpy(rows).cuda()]), y64, abs64, "nk ffn prefill")
+
+
 @pytest.mark.parametrize("M", list(range(1, 18)) + [23, 24, 25, 31, 32])
 def test_nk_small_m(M):
     """M <= 32 with [N, K] weights.  The LDS-DMA kernel (64 W rows per block,

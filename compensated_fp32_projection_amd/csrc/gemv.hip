@@ -672,10 +672,11 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 //
 // Every output column streams its own row of W, so the 1 KiB pieces that
 // stream fastest lie along K and no partial sums cross blocks: one dispatch.
-// A block (8 waves) owns 64 W rows (output columns) over all of K and walks
-// them in stages of 32 KiB through the four-buffer LDS ring: stage s holds
-// rows 32 (s & 1) .. + 31 of the block at k = 512 (s >> 1) .. + 511, one
-// whole 1 KiB piece of each row, each piece one LDS-DMA load (streaming
+// A block (8 waves) owns up to 64 W rows (output columns; 48, 56 or 64 as
+// the launcher picks, the stage rows past them load zeros) over all of K
+// and walks them in stages of 32 KiB through the four-buffer LDS ring:
+// stage s holds rows 32 (s & 1) .. + 31 of the block at k = 512 (s >> 1)
+// .. + 511, one whole 1 KiB piece of each row, each piece one LDS-DMA load (streaming
 // cache policy: every byte of W is read once).  Row r of a stage keeps its
 // granule g at slot 64 r + (g ^ (r % 16)), so the 16 rows an MFMA B fragment
 // reads at one granule fall in 16 different bank groups, and a B fragment is
@@ -684,7 +685,8 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 // above) are loaded one piece ahead and serve both row halves.  At the end
 // the waves' sums are added in wave order through LDS, and the lane that
 // holds both rows of an output merges it (and adds the bias).  Measured at
-// 1..8 x 4096 x 14336 with W streamed from HBM: 23.6-24.6 us, against
+// 1..8 x 4096 x 14336 with W streamed from HBM and 64-row blocks:
+// 23.6-24.6 us (56-row blocks, below: 22.4-22.6 us at M = 1), against
 // 27-36 us for 16 waves per 16 columns loading their B fragments straight
 // from memory (64-byte pieces of each row per wave instruction); 4 or 16
 // waves per block, and walking one row half through all of K before the
@@ -707,11 +709,13 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
                                                                 const uint16_t *__restrict__ w, int64_t ldw,
                                                                 float *__restrict__ y, int64_t ldy,
                                                                 const float *__restrict__ bias, int M, int64_t N,
-                                                                int64_t K)
+                                                                int64_t K, int rows)
 {
+    // The block owns W rows n0 .. n0 + rows - 1 (rows <= 64, a multiple of
+    // 8); stage rows from `rows` up load zeros and are not written.
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n0 = (int64_t)blockIdx.x * kNkRows;
+    const int64_t n0 = (int64_t)blockIdx.x * rows;
     const int pieces = (int)((K + kNkPiece - 1) / kNkPiece);
     const int nst = 2 * pieces;
 
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t n = n0 + 32 * h + r;
-            w_base[h][j] = n < N ? (int)((n * ldw + 8 * gr) * 2) : -1;
+            w_base[h][j] = 32 * h + r < rows && n < N ? (int)((n * ldw + 8 * gr) * 2) : -1;
         }
     }
     auto issue = [&](auto buf_tag, int s) __attribute__((always_inline)) {
@@ -856,6 +860,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     __syncthreads();
     const int b = (threadIdx.x >> 6) & 3;
     const int64_t n = n0 + 16 * b + (lane & 15);
+    const bool own = 16 * b + (lane & 15) < rows && n < N;
     for (int q = threadIdx.x >> 8; q < G; q += 64 * kNkWaves / 256) {
         const floatx4_t *rq = red(q);
         floatx4_t t = rq[b * 64 + lane];
@@ -864,7 +869,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 #pragma unroll
             for (int e = 0; e < 4; ++e) t[e] += u[e];
         }
-        if (n >= N) continue;
+        if (!own) continue;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int m = 8 * q + 2 * kq + h;
@@ -1077,17 +1082,32 @@ hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_
                       ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x)) & 15) == 0 &&
                       N * ldw * 2 < kLimit && M * ldx * 4 < kLimit && K < kLimit / 64;
     if (fast) {
-        const int64_t blocks = (N + kNkRows - 1) / kNkRows;
+        // 64, 56 or 48 rows per block, whichever leaves the fewest rows to
+        // the busiest CU (ties: more rows).  A block streams at a rate of
+        // its own, so the rows a CU must stream set the time: measured with
+        // M = 1, K = 4096, N = 4096 / 12288 / 14336 / 57344 take 14.7 / 19.5
+        // / 22.5 / 76.6 us (48, 48, 56, 56 rows) against 16.0 / 21.9 / 23.4
+        // / 84.4 us with 64.  Each output's k order is the same either way.
+        int rows = kNkRows;
+        int64_t busiest = INT64_MAX;
+        for (int r = kNkRows; r >= 48; r -= 8) {
+            const int64_t per_cu = ((N + r - 1) / r + kTargetBlocks - 1) / kTargetBlocks * r;
+            if (per_cu < busiest) {
+                busiest = per_cu;
+                rows = r;
+            }
+        }
+        const int64_t blocks = (N + rows - 1) / rows;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (M <= kGemvMaxRows)
             gemv_nk_kernel<1><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
-                                                                                   (int)M, N, K);
+                                                                                   (int)M, N, K, rows);
         else if (M <= 2 * kGemvMaxRows)
             gemv_nk_kernel<2><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
-                                                                                   (int)M, N, K);
+                                                                                   (int)M, N, K, rows);
         else
             gemv_nk_kernel<4><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
-                                                                                   (int)M, N, K);
+                                                                                   (int)M, N, K, rows);
         return hipGetLastError();
     }
     if (M > kGemvMaxRows) return hipErrorNotSupported;  // the GEMM path takes it

@@ -122,15 +122,16 @@ def test_nk_ffn_prefill_full_size_matches_kn():
 
 @pytest.mark.parametrize("M", list(range(1, 18)) + [23, 24, 25, 31, 32])
 def test_nk_small_m(M):
-    """M <= 32 with [N, K] weights.  The LDS-DMA kernel (64 W rows per block,
-    1 KiB pieces of K; one, two or four groups of 8 rows of x): the full decode
-    shape, K below one piece (down to one granule), exactly one piece, a
-    ragged last piece, an odd number of pieces with a padded row stride, 16
-    pieces, and N with a partial last block (down to one row).  K % 8 != 0 and unaligned weights
+    """M <= 32 with [N, K] weights.  The LDS-DMA kernel (48, 56 or 64 W rows
+    per block, 1 KiB pieces of K; one, two or four groups of 8 rows of x):
+    the full decode shape (56-row blocks), K below one piece (down to one
+    granule), exactly one piece, a ragged last piece, an odd number of pieces
+    with a padded row stride, 16 pieces, N with a partial last block (down to
+    one row), and partial last blocks of 56, 48 and 64 rows.  K % 8 != 0 and unaligned weights
     take the generic kernel (M <= 8) or the GEMM path."""
     cases = [(4096, 14336, 0, 0), (1000, 777, 0, 0), (256, 100, 0, 0), (512, 65, 0, 0), (1536, 130, 0, 8),
              (8192, 200, 0, 0), (8, 1, 0, 0), (16, 3, 0, 0), (1001, 64, 0, 0), (64, 33, 1, 0), (8, 1, 0, 3),
-             (96, 520, 0, 5)]
+             (96, 520, 0, 5), (1024, 13000, 0, 0), (520, 10300, 0, 0), (264, 15999, 0, 0)]
     for K, N, w_off, w_pad in cases:
         A, W = workloads.random_case(M * 100 + K + N, M, K, N, a_scale=30.0)
         note(f"linear_ex nk small M={M} K={K} N={N} w_off={w_off} w_pad={w_pad}")

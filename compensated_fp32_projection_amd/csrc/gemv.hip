@@ -704,7 +704,22 @@ static_assert(kNkRows / 2 * (kNkPiece / 8) == kWSlots, "a stage fills one ring b
 
 __device__ __forceinline__ int nk_slot(int r, int g) { return r * (kNkPiece / 8) + (g ^ (r & 15)); }
 
-template <int G>
+// ONE (M = 1, G = 1): each wave brings its 64 values of x per piece into
+// LDS with one 4-byte LDS-DMA load per lane (instead of four 16-byte loads
+// per lane into registers, seven of every eight lanes of which read rows
+// past M), into the slot of the piece's parity, and builds its A operands
+// from there.  Measured at M = 1, K = 4096: N = 14336 / 57344 in 22.3 /
+// 75.0-75.5 us against 23.1-23.4 / 77.2-78.6 us with the register loads.
+__shared__ uint4 g_nkx0[kNkWaves * 16];  // x of even pieces: 64 floats per wave
+__shared__ uint4 g_nkx1[kNkWaves * 16];  // x of odd pieces
+template <int P>
+__device__ __forceinline__ uint4 *nk_xslot()
+{
+    if constexpr (P == 0) return g_nkx0;
+    else return g_nkx1;
+}
+
+template <int G, bool ONE = false>
 __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__restrict__ x, int64_t ldx,
                                                                 const uint16_t *__restrict__ w, int64_t ldw,
                                                                 float *__restrict__ y, int64_t ldy,
@@ -713,6 +728,8 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 {
     // The block owns W rows n0 .. n0 + rows - 1 (rows <= 64, a multiple of
     // 8); stage rows from `rows` up load zeros and are not written.
+    static_assert(!ONE || G == 1, "one row of x is one group");
+    constexpr int kXLoadsPerPiece = ONE ? 1 : G * kNkXLoads;  // per wave
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * rows;
@@ -762,6 +779,13 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     // x of one piece: read into the A operands at the start of an even
     // stage, then overwritten by the next piece's loads.
     floatx4_t xs[G][kNkSteps][2];
+    // ONE: lane l of the wave loads x[0][512 p + 64 wave + l] into slot p % 2.
+    auto load_x1 = [&](auto slot_tag, int p) __attribute__((always_inline)) {
+        const int k = kNkPiece * p + 32 * kNkSteps * wave + lane;
+        const int o = p < pieces && k < (int)K ? 4 * k : kNoOffset;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(nk_xslot<decltype(slot_tag)::value>() + 16 * wave),
+                                                 4, o, 0, 0, 0);
+    };
     auto load_x = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < G; ++q)
@@ -776,6 +800,22 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
             }
     };
     half8_t af[G][kNkSteps];
+    // ONE: lane l wants values 32 t + 8 kq .. + 7 of the wave's 64 (granules
+    // 8 t + 2 kq and + 1 of its slot); only x row 0 (i = 0, 1) is live.
+    auto build_a1 = [&](auto slot_tag) __attribute__((always_inline)) {
+        const uint4 *xb = nk_xslot<decltype(slot_tag)::value>() + 16 * wave;
+#pragma unroll
+        for (int t = 0; t < kNkSteps; ++t) {
+            const floatx4_t v0 = __builtin_bit_cast(floatx4_t, xb[8 * t + 2 * kq]);
+            const floatx4_t v1 = __builtin_bit_cast(floatx4_t, xb[8 * t + 2 * kq + 1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                _Float16 h, l;
+                split_value(e < 4 ? v0[e] : v1[e - 4], h, l);
+                af[0][t][e] = am == 0 ? (a_lo ? l : h) : (_Float16)0.0f;
+            }
+        }
+    };
     auto build_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < G; ++q)
@@ -805,8 +845,13 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
         constexpr int S = decltype(buf_tag)::value;
         const uint4 *buf = wring<S>();
         if constexpr ((S & 1) == 0) {
-            build_a();
-            load_x((s >> 1) + 1);
+            if constexpr (ONE) {  // piece s / 2 sits in slot (S / 2) % 2 (s = S mod 4)
+                build_a1(std::integral_constant<int, (S >> 1) & 1>{});
+                load_x1(std::integral_constant<int, ((S >> 1) + 1) & 1>{}, (s >> 1) + 1);
+            } else {
+                build_a();
+                load_x((s >> 1) + 1);
+            }
         }
         half8_t bf[kNkSteps][2];
 #pragma unroll
@@ -825,11 +870,14 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
                 for (int q = 0; q < G; ++q)
                     acc[q][2 * (S & 1) + jb] =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(af[q][t], bf[t][jb], acc[q][2 * (S & 1) + jb], 0, 0, 0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((S & 1) ? 2 * kNkLoads : 2 * kNkLoads + G * kNkXLoads));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((S & 1) ? 2 * kNkLoads : 2 * kNkLoads + kXLoadsPerPiece));
         __builtin_amdgcn_s_barrier();
     };
 
-    load_x(0);
+    if constexpr (ONE)
+        load_x1(std::integral_constant<int, 0>{}, 0);
+    else
+        load_x(0);
     issue(std::integral_constant<int, 0>{}, 0);
     issue(std::integral_constant<int, 1>{}, 1);
     issue(std::integral_constant<int, 2>{}, 2);
@@ -1099,7 +1147,10 @@ hipError_t launch_gemv_nk(const float *x, int64_t ldx, const uint16_t *w, int64_
         }
         const int64_t blocks = (N + rows - 1) / rows;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        if (M <= kGemvMaxRows)
+        if (M == 1)
+            gemv_nk_kernel<1, true><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy,
+                                                                                         bias, 1, N, K, rows);
+        else if (M <= kGemvMaxRows)
             gemv_nk_kernel<1><<<dim3((unsigned)blocks), 64 * kNkWaves, 0, stream>>>(x, ldx, w, ldw, y, ldy, bias,
                                                                                    (int)M, N, K, rows);
         else if (M <= 2 * kGemvMaxRows)

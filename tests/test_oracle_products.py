@@ -206,3 +206,106 @@ def test_y64_at_matches_full_product_on_workload():
     ys, abss = oracle.y64_at(A, W, r, c)
     assert np.allclose(ys, y64[r, c], rtol=0, atol=1e-12 * abss.max())
     assert np.allclose(abss, abs64[r, c], rtol=1e-12, atol=0)
+
+
+# -- O5(b) and O5(c): the FP32 roundings themselves --------------------------------
+#
+# The exact-integer cases above are exact in FP32 and FP64 alike, so they do
+# not tell FP32 accumulation from FP64 accumulation.  The cases below use
+# inputs where FP32 rounds at almost every step, and restate each product
+# independently: numpy float32 arithmetic for the method's sums, and float64
+# arithmetic on ranges where it is exact (or exact rationals) for the fused
+# multiply-add.  A change to either accumulator's precision or to the order
+# of its roundings fails them.
+
+def _np_split(A):
+    """The split restated with numpy casts (RNE, subnormals kept): hi is the
+    float16 cast of x, the residual x - hi is exact in float32, lo the cast of
+    1024 times it."""
+    hi = A.astype(np.float16)
+    r = A - hi.astype(np.float32)
+    lo = (r * np.float32(1024.0)).astype(np.float16)
+    return hi, lo
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(6, 300, 37, 1), (3, 1000, 5, 2), (1, 4096, 64, 3)])
+def test_linear_cf32_fp32_sums_bitwise(M, K, N, seed):
+    """C_hi, C_lo and y of the method on the CPU equal a numpy float32
+    restatement bit for bit: each FP16 x FP16 product is exact in float32,
+    each partial sum is one float32 addition with k ascending, and the merge
+    is two float32 operations after both sums are complete."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K), dtype=np.float32)
+    W = (rng.standard_normal((K, N), dtype=np.float32) * np.float32(0.05)).astype(np.float16)
+    hi, lo = _np_split(A)
+    h32, l32, w32 = hi.astype(np.float32), lo.astype(np.float32), W.astype(np.float32)
+    sh = np.zeros((M, N), np.float32)
+    sl = np.zeros((M, N), np.float32)
+    for k in range(K):
+        sh = sh + np.outer(h32[:, k], w32[k])
+        sl = sl + np.outer(l32[:, k], w32[k])
+    y = sh + sl * np.float32(2.0 ** -10)
+    got_y, got_h, got_l = oracle.linear_cf32(A, W)
+    assert np.array_equal(got_h.view(np.uint32), sh.view(np.uint32))
+    assert np.array_equal(got_l.view(np.uint32), sl.view(np.uint32))
+    assert np.array_equal(got_y.view(np.uint32), y.view(np.uint32))
+    # The sums really are rounded: float64 accumulation of the same exact
+    # products differs in most positions, so such a change could not pass.
+    sh64 = h32.astype(np.float64) @ w32.astype(np.float64)
+    assert np.count_nonzero(sh64.astype(np.float32) != sh) > M * N // 4
+
+
+def _rne_f32(q: Fraction) -> np.float32:
+    """The float32 nearest to the rational q, ties to the even significand."""
+    f = np.float32(float(q))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - q)
+        if best is None or d < best[0] or (d == best[0] and (int(c.view(np.uint32)) & 1) == 0):
+            best = (d, c)
+    return np.float32(best[1])
+
+
+def test_linear_f32_fused_steps_exact_rationals():
+    """The plain FP32 product on unrestricted N(0,1) x N(0,0.05) inputs: each
+    step is acc <- RNE32(a w + acc), the exact rational a w + acc rounded once
+    (a fused multiply-add), k ascending."""
+    rng = np.random.default_rng(9)
+    M, K, N = 2, 48, 3
+    A = rng.standard_normal((M, K), dtype=np.float32)
+    W = (rng.standard_normal((K, N), dtype=np.float32) * np.float32(0.05)).astype(np.float16)
+    got = oracle.linear_f32(A, W)
+    for i in range(M):
+        for j in range(N):
+            acc = np.float32(0.0)
+            for k in range(K):
+                acc = _rne_f32(Fraction(float(A[i, k])) * Fraction(float(W[k, j])) + Fraction(float(acc)))
+            assert got[i, j].view(np.uint32) == acc.view(np.uint32), (i, j)
+
+
+def test_linear_f32_fused_steps_bitwise():
+    """The same at a larger size, restated in float64: with |a| in [1, 16) and
+    |w| in [1/16, 1], every product a w and every partial sum is a multiple of
+    2^-37 below 2^14 in magnitude, so acc + a w is exact in float64 and one
+    cast to float32 is the single rounding of the fused multiply-add.  The
+    unfused form (product rounded to FP32 first) and float64 accumulation
+    both differ from it, so neither could pass."""
+    rng = np.random.default_rng(10)
+    M, K, N = 7, 300, 33
+    sign = rng.choice([-1.0, 1.0], (M, K))
+    A = (sign * (1.0 + rng.random((M, K))) * np.exp2(rng.integers(0, 4, (M, K)))).astype(np.float32)
+    W = ((1.0 + rng.random((K, N))) * np.exp2(rng.integers(-4, 0, (K, N)))
+         * rng.choice([-1.0, 1.0], (K, N))).astype(np.float16)
+    a64, w64 = A.astype(np.float64), W.astype(np.float64)
+    assert (np.abs(a64) >= 1).all() and (np.abs(a64) < 16).all()
+    assert (np.abs(w64) >= 1 / 16).all() and (np.abs(w64) <= 1).all()
+    acc = np.zeros((M, N), np.float32)
+    unfused = np.zeros((M, N), np.float32)
+    a32, w32 = A, W.astype(np.float32)
+    for k in range(K):
+        acc = (acc.astype(np.float64) + np.outer(a64[:, k], w64[k])).astype(np.float32)
+        unfused = unfused + np.outer(a32[:, k], w32[k])
+    got = oracle.linear_f32(A, W)
+    assert np.array_equal(got.view(np.uint32), acc.view(np.uint32))
+    assert np.count_nonzero(unfused != acc) > 0
+    assert np.count_nonzero((a64 @ w64).astype(np.float32) != acc) > M * N // 4

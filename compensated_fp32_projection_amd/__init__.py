@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcfp32.so")
@@ -257,21 +258,53 @@ def merge(c_hi, c_lo, y=None, stream=None):
 
 
 class Workspace:
-    """Grow-only device scratch for ``linear`` (one per stream of use)."""
+    """Grow-only device scratch for ``linear`` and ``linear_geglu``.
+
+    The library's kernels read and write the workspace asynchronously, in the
+    order of the stream they are launched on, so one Workspace serves one
+    stream at a time: calls on different streams that may overlap need one
+    each (the helpers' default keeps one per device and stream).  The buffer
+    is marked as used by every stream it is handed to (``record_stream``), so
+    when it grows, the caching allocator does not give the old buffer to
+    anyone else before the work queued on those streams is done."""
 
     def __init__(self):
         self.buf = None
+        self._lock = threading.Lock()
 
-    def get(self, nbytes, device):
+    def get(self, nbytes, device, stream=None):
         torch = _torch()
         if nbytes == 0:
             return None
-        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        return self.buf
+        with self._lock:
+            if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+                self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            buf = self.buf
+        if stream is not None and hasattr(stream, "cuda_stream"):
+            buf.record_stream(stream)
+        return buf
 
 
-_default_ws = Workspace()
+_default_lock = threading.Lock()
+_default_ws: dict = {}
+
+
+def _default_workspace(device, stream) -> Workspace:
+    """The helpers' own workspace for (device, stream): calls on different
+    streams never share scratch memory."""
+    key = (device.index if device.index is not None else -1, _stream(stream))
+    with _default_lock:
+        ws = _default_ws.get(key)
+        if ws is None:
+            ws = _default_ws[key] = Workspace()
+        return ws
+
+
+def _stream_obj(stream):
+    """The torch stream a helper call runs on (the current one by default)."""
+    if stream is None:
+        return _torch().cuda.current_stream()
+    return stream
 
 
 def linear(x, w, out=None, workspace: Workspace | None = None, stream=None, bias=None, w_layout: str = "kn"):
@@ -299,9 +332,10 @@ def linear(x, w, out=None, workspace: Workspace | None = None, stream=None, bias
         raise ValueError("out has the wrong shape")
     layout = W_KN if w_layout == "kn" else W_NK
     need = cfp32_linear_ex_workspace_bytes(M, N, K, layout)
-    ws = (workspace or _default_ws).get(need, x.device)
+    st = _stream_obj(stream)
+    ws = (workspace or _default_workspace(x.device, st)).get(need, x.device, st)
     pws = ws.data_ptr() if ws is not None else None
-    _check(cfp32_linear_ex(px, ldx, pw, ldw, layout, pb, py, ldy, M, N, K, pws, need, _stream(stream)),
+    _check(cfp32_linear_ex(px, ldx, pw, ldw, layout, pb, py, ldy, M, N, K, pws, need, _stream(st)),
            "cfp32_linear_ex")
     return out
 
@@ -327,9 +361,10 @@ def linear_geglu(x, w, bias=None, out=None, workspace: Workspace | None = None, 
     if (M3, F3) != (M, F):
         raise ValueError("out has the wrong shape")
     need = cfp32_linear_geglu_workspace_bytes(M, F, K)
-    ws = (workspace or _default_ws).get(need, x.device)
+    st = _stream_obj(stream)
+    ws = (workspace or _default_workspace(x.device, st)).get(need, x.device, st)
     pws = ws.data_ptr() if ws is not None else None
-    _check(cfp32_linear_geglu(px, ldx, pw, ldw, pb, po, ldo, M, F, K, pws, need, _stream(stream)),
+    _check(cfp32_linear_geglu(px, ldx, pw, ldw, pb, po, ldo, M, F, K, pws, need, _stream(st)),
            "cfp32_linear_geglu")
     return out
 

@@ -32,6 +32,7 @@
 //     pointer and leading dimension allow it, element loads otherwise.
 #include "device_common.h"
 #include "launchers.h"
+#include "tile_order.h"
 
 namespace cfp32 {
 
@@ -40,8 +41,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBK = 64;        // k per stage
 constexpr int kKG = kBK / 8;   // k-granules per stage
-constexpr int kGroupM = 4;     // tile-rows per scheduling group
-constexpr int kXcds = 8;       // XCDs on MI355X; blocks are dealt to them round-robin
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
@@ -142,17 +141,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
     const int64_t nbn = (g.N + T::BN - 1) / T::BN;
     const int64_t total = nbm * nbn;
     const int64_t chunk = (int64_t)blockIdx.x / total;  // 0 unless K is split
-    int64_t bid = (int64_t)blockIdx.x % total;
-    {
-        const int64_t q = total / kXcds, r = total % kXcds;
-        const int64_t xcd = bid % kXcds, local = bid / kXcds;
-        bid = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
-    }
-    const int64_t group_span = (int64_t)kGroupM * nbn;
-    const int64_t first_m = (bid / group_span) * kGroupM;
-    const int64_t gsize = (nbm - first_m) < kGroupM ? (nbm - first_m) : kGroupM;
-    const int64_t tile_m = first_m + (bid % group_span) % gsize;
-    const int64_t tile_n = (bid % group_span) / gsize;
+    int64_t tile_m, tile_n;
+    tile_of_block((int64_t)blockIdx.x % total, nbm, nbn, tile_m, tile_n);
     const int64_t m0 = tile_m * T::BM;
     const int64_t n0 = tile_n * T::BN;
 

@@ -871,7 +871,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
                     acc[q][2 * (S & 1) + jb] =
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(af[q][t], bf[t][jb], acc[q][2 * (S & 1) + jb], 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((S & 1) ? 2 * kNkLoads : 2 * kNkLoads + kXLoadsPerPiece));
-        __builtin_amdgcn_s_barrier();
+        block_barrier();
     };
 
     if constexpr (ONE)
@@ -882,7 +882,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     issue(std::integral_constant<int, 1>{}, 1);
     issue(std::integral_constant<int, 2>{}, 2);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kNkLoads));  // x of piece 0 and stage 0 landed
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
     for (int s = 0; s < nst; s += 4) {  // nst is even
         stage(std::integral_constant<int, 0>{}, s);
         stage(std::integral_constant<int, 1>{}, s + 1);
@@ -892,7 +892,19 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
         }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the trailing zero loads, before the ring is reused
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!ONE) {
+        // The wait counts above count the x register loads of every even
+        // stage.  A load whose value is never read may be deleted by the
+        // compiler (the last piece's loads are read by nobody), and then the
+        // counts would no longer hold back the W stage a wave reads next;
+        // reading the registers here keeps every one of those loads issued,
+        // whatever shape the stage loop is given.
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int t = 0; t < kNkSteps; ++t) asm volatile("" ::"v"(xs[q][t][0]), "v"(xs[q][t][1]));
+    }
+    block_barrier();
 
     // The waves' sums, [wave][block][lane] in ring buffer q for group q,
     // added in wave order.  16x16 accumulator: rows 4 kq + e, column

@@ -27,7 +27,7 @@ CASES = [("kn", 1, 4096, 3584), ("nk", 3, 2048, 1536), ("kn", 40, 1024, 2048), (
 
 
 class Job:
-    def __init__(self, idx, kind, M, K, N):
+    def __init__(self, idx, kind, M, K, N, own_workspace=True):
         A, W = workloads.random_case(1000 + idx, M, K, N, a_scale=8.0)
         self.kind = kind
         self.x = to_dev(A)
@@ -35,7 +35,7 @@ class Job:
         self.w = to_dev(w).view(torch.float16)
         cols = N // 2 if kind == "geglu" else N
         self.out = torch.full((M, cols), 3.0, dtype=torch.float32, device="cuda")
-        self.ws = cf.Workspace()
+        self.ws = cf.Workspace() if own_workspace else None
 
     def run(self, stream=None):
         if self.kind == "geglu":
@@ -112,3 +112,23 @@ def test_two_host_threads():
     assert not errors, errors
     torch.cuda.synchronize()
     check(jobs, want, "threads")
+
+
+def test_many_streams_default_workspace():
+    """The tensor helpers' own workspace (no ``workspace=`` given): one per
+    device and stream, so jobs on different streams in flight together never
+    share scratch memory, and each gives the bits of its serial run."""
+    jobs = [Job(i, *c, own_workspace=False) for i, c in enumerate(CASES)]
+    note("concurrent streams, default workspace: serial pass")
+    want = serial_results(jobs)
+    for j in jobs:
+        j.out.fill_(3.0)
+    streams = [torch.cuda.Stream() for _ in jobs]
+    torch.cuda.synchronize()
+    note(f"concurrent streams, default workspace: {len(jobs)} streams x 3 rounds")
+    for _ in range(3):
+        for j, s in zip(jobs, streams):
+            with torch.cuda.stream(s):
+                j.run(stream=s)
+    torch.cuda.synchronize()
+    check(jobs, want, "streams, default workspace")

@@ -72,3 +72,37 @@ def assert_better_than_single(y, c_hi, y64, abs64, what=""):
     assert ymax * RATIO <= smax, f"{what}: max error {ymax:.3g} not {RATIO}x below single-FP16 {smax:.3g}"
     assert yrms * RATIO <= srms, f"{what}: rms error {yrms:.3g} not {RATIO}x below single-FP16 {srms:.3g}"
     return ymax, smax
+
+
+def check_all_rows(A, W, y, c_hi=None, what="", block=1024):
+    """Every element of y [M, N] against the FP64 reference, a block of rows
+    at a time (the float64 products of a full 8192 x 4096 x 14336 output
+    would need several GB at once): tolerance, finiteness and exact zeros as
+    assert_within_tolerance.  With c_hi (the same call's single-FP16
+    product), also the 16x error ratio over the whole output.  Returns the
+    max and RMS normalised errors of y (and of c_hi, or None)."""
+    import oracle
+    M = A.shape[0]
+    ymax = ysq = 0.0
+    smax = ssq = 0.0
+    for r0 in range(0, M, block):
+        r1 = min(M, r0 + block)
+        y64, abs64 = oracle.y64(A[r0:r1], W)
+        yb = np.asarray(y[r0:r1])
+        assert_within_tolerance(yb, y64, abs64, f"{what} rows {r0}:{r1}")
+        den = np.where(abs64 > 0, abs64, 1.0)
+        e = np.abs(yb.astype(np.float64) - y64) / den
+        ymax = max(ymax, float(e.max()))
+        ysq += float(np.sum(e * e))
+        if c_hi is not None:
+            s = np.abs(np.asarray(c_hi[r0:r1], np.float64) - y64) / den
+            smax = max(smax, float(s.max()))
+            ssq += float(np.sum(s * s))
+    n = y.shape[0] * y.shape[1]
+    yrms = (ysq / n) ** 0.5
+    if c_hi is None:
+        return ymax, yrms, None, None
+    srms = (ssq / n) ** 0.5
+    assert ymax * RATIO <= smax, f"{what}: max error {ymax:.3g} not {RATIO}x below single-FP16 {smax:.3g}"
+    assert yrms * RATIO <= srms, f"{what}: rms error {yrms:.3g} not {RATIO}x below single-FP16 {srms:.3g}"
+    return ymax, yrms, smax, srms

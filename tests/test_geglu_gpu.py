@@ -9,7 +9,7 @@ applied to those FP32 columns, and the kernel may differ from it only by its
 FP32 GELU rounding: |out - ref| <= 2e-6 * |gate * up| (erff and four FP32
 roundings, about 32 ulp, with the scale of gelu(gate) * up bounded by
 |gate * up|).  The full-width projection itself is checked against the FP64
-reference on sampled rows, which ties the chain to the pinned oracle.
+reference on every row, which ties the chain to the pinned oracle.
 """
 import numpy as np
 import pytest
@@ -18,7 +18,7 @@ import torch
 import compensated_fp32_projection_amd as cf
 import oracle
 from compensated_fp32_projection_amd import workloads
-from gpu_helpers import assert_within_tolerance, note, stream_handle, to_dev, to_host
+from gpu_helpers import assert_within_tolerance, check_all_rows, note, stream_handle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def test_geglu_paths(M, K, F, with_bias):
     check_geglu(out, y_full, F, f"{M}x{K}x{F}")
     out2 = run_geglu(A, W, bias)
     assert np.array_equal(out.view(np.uint32), out2.view(np.uint32)), "not deterministic"
-    rows = np.arange(M) if M <= 32 else np.random.default_rng(M).choice(M, 32, replace=False)
+    rows = np.arange(M)
     y64, abs64 = oracle.y64(A[rows], W)
     if bias is not None:
         # The bias addition rounds once more, by at most 2^-24 |y|; widen the
@@ -113,16 +113,19 @@ def test_geglu_unaligned_weight_fallback(M):
     check_geglu(out, full_projection(A, W, w_offset=1), F, f"unaligned M={M}")
 
 
-def test_geglu_ffn_prefill_shape_sampled():
-    """The FFN shape: x [8192, 4096], W [4096, 14336] as gate | up (F = 7168)."""
+def test_geglu_ffn_prefill_full_size():
+    """The FFN shape: x [8192, 4096], W [4096, 14336] as gate | up (F = 7168),
+    the fused GEMM epilogue: every output against the oracle's GEGLU of the
+    projection's gate and up columns, and every projection output against
+    the FP64 reference."""
     wl = workloads.decode_ffn_pair()
     A, W = wl.A[1], wl.W
     F = W.shape[1] // 2
     note("geglu ffn prefill 8192x4096x7168")
     out = run_geglu(A, W)
     y_full = full_projection(A, W)
-    rows = np.random.default_rng(3).choice(A.shape[0], 256, replace=False)
-    check_geglu(out[rows], y_full[rows], F, "ffn prefill")
+    check_geglu(out, y_full, F, "ffn prefill")
+    check_all_rows(A, W, y_full, None, "ffn prefill projection")
 
 
 def test_geglu_k_zero():

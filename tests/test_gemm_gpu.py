@@ -8,8 +8,9 @@ For every workload and for random shapes that cut every tile edge:
     exact value (which also catches swapped or mis-scaled parts);
   * y's error is at least 16x below that of the single-FP16 product C_hi;
   * a repeated call gives identical bits.
-At the full 8192 x 4096 x 14336 size the FP64 reference is taken at sampled
-positions; the merge identity and determinism are checked everywhere.
+At the full 8192 x 4096 x 14336 size every element is checked against the
+FP64 reference too (a block of rows at a time), with the 16x ratio against
+the same launch's C_hi over the whole output.
 """
 import numpy as np
 import pytest
@@ -18,8 +19,8 @@ import torch
 import compensated_fp32_projection_amd as cf
 import oracle
 from compensated_fp32_projection_amd import workloads
-from gpu_helpers import (TOL, assert_better_than_single, assert_within_tolerance, note, rel_errors,
-                         stream_handle, to_dev, to_host)
+from gpu_helpers import (TOL, assert_better_than_single, assert_within_tolerance, check_all_rows, note,
+                         rel_errors, stream_handle, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -199,25 +200,24 @@ def test_mfma_accumulation_drift_is_bounded():
 
 
 def test_gemm_decode_ffn_prefill_full_size():
-    """8192 x 4096 x 14336: y at 8192 sampled positions against FP64, the merge
-    identity on all 117M outputs, and determinism."""
+    """8192 x 4096 x 14336, the FFN projection the benchmark times (split +
+    the LDS-DMA GEMM): every one of the 117M outputs within 1e-5 * sum|a w|
+    of FP64, the error 16x below the same launch's single-FP16 C_hi over the
+    whole output, the merge identity everywhere, and determinism."""
     wl = workloads.decode_ffn_pair()
     A, W = wl.A[1], wl.W
-    M, K = A.shape
-    N = W.shape[1]
     note("gemm decode_ffn prefill full size")
     hi_t, lo_t = cf.split(to_dev(A))
     dw = to_dev(W)
     y, ch, cl = cf.gemm(hi_t, lo_t, dw, want_y=True, want_parts=True)
     yh = to_host(y)
-    merged = oracle.merge(to_host(ch), to_host(cl))
+    chh = to_host(ch)
+    merged = oracle.merge(chh, to_host(cl))
     assert np.array_equal(merged.view(np.uint32), yh.view(np.uint32))
     del ch, cl, merged
-    rng = np.random.default_rng(11)
-    r = rng.integers(0, M, 8192)
-    c = rng.integers(0, N, 8192)
-    y64, abs64 = oracle.y64_at(A, W, r, c)
-    assert_within_tolerance(yh[r, c], y64, abs64, "prefill sampled")
+    ymax, yrms, smax, srms = check_all_rows(A, W, yh, chh, "prefill 8192x4096x14336")
+    print(f"prefill full size: y max {ymax:.3g} rms {yrms:.3g}; C_hi max {smax:.3g} rms {srms:.3g}")
+    del chh
     y2, _, _ = cf.gemm(hi_t, lo_t, dw, want_y=True, want_parts=False)
     assert torch.equal(y, y2)
 
@@ -350,6 +350,4 @@ def test_linear_fused_split_matches_two_launches(M, K, N):
     assert cf.cfp32_gemm(hi.data_ptr(), lo.data_ptr(), K, dw.data_ptr(), N, y2.data_ptr(), None, None, N,
                          M, N, K, stream_handle()) == cf.OK
     assert np.array_equal(y.view(np.uint32), to_host(y2).view(np.uint32))
-    rows = np.random.default_rng(M).choice(M, size=min(M, 512), replace=False)
-    y64, abs64 = oracle.y64(A[rows], W)
-    assert_within_tolerance(y[rows], y64, abs64, f"fused {M}x{K}x{N}")
+    check_all_rows(A, W, y, None, f"fused {M}x{K}x{N}")

@@ -19,7 +19,7 @@ import torch
 import compensated_fp32_projection_amd as cf
 import oracle
 from compensated_fp32_projection_amd import workloads
-from gpu_helpers import assert_within_tolerance, note, stream_handle, to_dev, to_host
+from gpu_helpers import assert_better_than_single, assert_within_tolerance, check_all_rows, note, stream_handle, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_bias_is_one_fp32_addition(M, K, N, layout):
     y0 = run_ex(A, W, layout)
     y1 = run_ex(A, W, layout, bias)
     assert np.array_equal(y1.view(np.uint32), (y0 + bias[None, :]).astype(np.float32).view(np.uint32))
-    rows = np.arange(M) if M <= 64 else np.random.default_rng(M).choice(M, 64, replace=False)
+    rows = np.arange(M)
     y64, abs64 = oracle.y64(A[rows], W)
     assert_within_tolerance(y0[rows], y64, abs64, f"{M}x{K}x{N} layout={layout}")
 
@@ -94,7 +94,8 @@ def test_nk_matches_kn_bitwise_above_32_rows(M, K, N):
 def test_nk_ffn_prefill_full_size_matches_kn():
     """The FFN projection 8192 x 4096 x 14336 with the weights in both
     layouts (the [N, K] GEMM with 64-deep W stages, as bench.py times it):
-    the same bits everywhere, and the FP64 reference at sampled rows."""
+    the same bits everywhere, and every element within tolerance of the FP64
+    reference."""
     wl = workloads.decode_ffn_pair()
     A, W = wl.A[1], wl.W
     M, K = A.shape
@@ -115,9 +116,7 @@ def test_nk_ffn_prefill_full_size_matches_kn():
         outs.append(y)
         del ws
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32)), "[N, K] and [K, N] differ"
-    rows = np.random.default_rng(11).choice(M, 48, replace=False)
-    y64, abs64 = oracle.y64(A[rows], W)
-    assert_within_tolerance(to_host(outs[1][torch.from_numpy(rows).cuda()]), y64, abs64, "nk ffn prefill")
+    check_all_rows(A, W, to_host(outs[1]), None, "nk ffn prefill")
 
 
 @pytest.mark.parametrize("M", list(range(1, 18)) + [23, 24, 25, 31, 32])
@@ -138,6 +137,11 @@ def test_nk_small_m(M):
         y = run_ex(A, W, cf.W_NK, w_offset=w_off, w_ld_pad=w_pad)
         y64, abs64 = oracle.y64(A, W)
         assert_within_tolerance(y, y64, abs64, f"nk M={M} K={K} N={N}")
+        # "measurably below a single FP16 conversion": this kernel does not
+        # expose its C_hi, so the oracle's FP32 C_hi of the same inputs is
+        # the single-conversion product
+        _, ch, _ = oracle.linear_cf32(A, W)
+        assert_better_than_single(y, ch, y64, abs64, f"nk M={M} K={K} N={N}")
         y2 = run_ex(A, W, cf.W_NK, w_offset=w_off, w_ld_pad=w_pad)
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
 

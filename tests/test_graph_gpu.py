@@ -7,7 +7,9 @@ The library records no memset and keeps no state between calls: the small-M
 path's workspace holds partial sums that every call rewrites before reading,
 and the M > 8 path's hi/lo planes likewise.  Each replay here is checked bit
 for bit against an eager call on the same inputs, with eager work and
-synchronisations between the replays.
+synchronisations between the replays -- also with the eager calls on the
+graph's own workspace, so that eager calls and replays alternate on one
+workspace.
 """
 import numpy as np
 import pytest
@@ -23,10 +25,11 @@ pytestmark = pytest.mark.gpu
 # [K, N] weights: the small-M product + merge dispatches, the generic small-M
 # kernel, split + GEMM.  [N, K] weights: the one-dispatch small-M kernel (one
 # and three groups of 8 rows) and the GEMM with 64-deep W stages.
+@pytest.mark.parametrize("shared_ws", [False, True])
 @pytest.mark.parametrize("M,K,N,layout", [(1, 4096, 14336, "kn"), (4, 1000, 520, "kn"), (2, 24, 40, "kn"),
-                                          (300, 512, 768, "kn"), (1, 4096, 14336, "nk"), (20, 1024, 3000, "nk"),
-                                          (300, 512, 768, "nk")])
-def test_linear_replays_match_eager(M, K, N, layout):
+                                          (12, 2048, 3000, "kn"), (300, 512, 768, "kn"), (1, 4096, 14336, "nk"),
+                                          (20, 1024, 3000, "nk"), (300, 512, 768, "nk")])
+def test_linear_replays_match_eager(M, K, N, layout, shared_ws):
     A, W = workloads.random_case(M + K + N, M, K, N, a_scale=4.0)
     dw = to_dev(W if layout == "kn" else np.ascontiguousarray(W.T)).view(torch.float16)
     x = to_dev(A)
@@ -49,7 +52,7 @@ def test_linear_replays_match_eager(M, K, N, layout):
         g.replay()
         torch.cuda.synchronize()
         got = to_host(y).copy()
-        ref = to_host(cf.linear(x, dw, workspace=cf.Workspace(), w_layout=layout))
+        ref = to_host(cf.linear(x, dw, workspace=ws if shared_ws else cf.Workspace(), w_layout=layout))
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"replay {r}"
 
 

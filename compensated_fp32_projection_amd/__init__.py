@@ -9,7 +9,7 @@ Low-level entry points carry the C names and take raw integers (device
 pointers, sizes, stream handle):
 
     cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
-    cfp32_linear, cfp32_linear_workspace_bytes, cfp32_linear_ex,
+    cfp32_linear, cfp32_linear_noalloc, cfp32_linear_workspace_bytes, cfp32_linear_ex,
     cfp32_linear_ex_workspace_bytes, cfp32_linear_geglu,
     cfp32_linear_geglu_workspace_bytes, cfp32_qkv_rotary, cfp32_status_string,
     cfp32_last_hip_error
@@ -28,7 +28,7 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcfp32.so")
 
-OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED_DEVICE, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED_DEVICE, ERR_HIP, ERR_TOO_LARGE = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "cfp32_status_string",
@@ -39,6 +39,7 @@ EXPORTS = (
     "cfp32_merge",
     "cfp32_linear_workspace_bytes",
     "cfp32_linear",
+    "cfp32_linear_noalloc",
     "cfp32_linear_ex_workspace_bytes",
     "cfp32_linear_ex",
     "cfp32_linear_geglu_workspace_bytes",
@@ -87,6 +88,8 @@ def load_library():
     lib.cfp32_linear_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.cfp32_linear.restype = I32
+    lib.cfp32_linear_noalloc.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.cfp32_linear_noalloc.restype = I32
     lib.cfp32_linear_ex_workspace_bytes.argtypes = [I64, I64, I64, I32]
     lib.cfp32_linear_ex_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear_ex.argtypes = [P, I64, P, I64, I32, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
@@ -134,6 +137,10 @@ def cfp32_linear_workspace_bytes(M, N, K) -> int:
 
 def cfp32_linear(x, ldx, w, ldw, y, ldy, M, N, K, workspace, workspace_bytes, stream) -> int:
     return int(load_library().cfp32_linear(x, ldx, w, ldw, y, ldy, M, N, K, workspace, workspace_bytes, stream))
+
+
+def cfp32_linear_noalloc(x, ldx, w, ldw, y, ldy, M, N, K, stream) -> int:
+    return int(load_library().cfp32_linear_noalloc(x, ldx, w, ldw, y, ldy, M, N, K, stream))
 
 
 def cfp32_linear_ex_workspace_bytes(M, N, K, w_layout) -> int:

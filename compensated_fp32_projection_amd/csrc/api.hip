@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/cfp32.h"
 #include "launchers.h"
@@ -75,6 +76,10 @@ int64_t split_ld(int64_t K) { return (K + 7) / 8 * 8; }
 
 size_t plane_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)split_ld(K) * 2u, kAlign); }
 
+cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, bool nk, const float *bias,
+                          float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, uintptr_t base, size_t need,
+                          hipStream_t s);
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +91,8 @@ const char *cfp32_status_string(cfp32_status s)
     case CFP32_ERR_INVALID_VALUE: return "invalid argument (null pointer, negative size, leading dimension or workspace too small)";
     case CFP32_ERR_UNSUPPORTED_DEVICE: return "no usable device: the current HIP device is not gfx950 (there is no CPU fallback)";
     case CFP32_ERR_HIP: return "HIP runtime error (see cfp32_last_hip_error)";
+    case CFP32_ERR_TOO_LARGE:
+        return "problem too large for the no-allocation entry point (its fixed scratch holds 64 MiB per device)";
     }
     return "unknown status";
 }
@@ -199,9 +206,21 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
     if (need > 0 && (!workspace || workspace_bytes < need)) return CFP32_ERR_INVALID_VALUE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
-    hipStream_t s = (hipStream_t)stream;
-
     const uintptr_t base = round_up(reinterpret_cast<uintptr_t>(workspace), kAlign);
+    return linear_paths(x, ldx, w, ldw, nk, bias, y, ldy, M, N, K, base, need, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The projection's paths, after validation, on a workspace at `base`
+// (256-byte aligned) holding at least need - kAlign bytes (need as
+// cfp32_linear_ex_workspace_bytes gives it, 0 when none is needed).
+cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, bool nk, const float *bias,
+                          float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, uintptr_t base, size_t need,
+                          hipStream_t s)
+{
     if (M <= cfp32::kGemvMaxRows && nk)
         return launched(cfp32::launch_gemv_nk(x, ldx, w, ldw, y, ldy, M, N, K, s, bias));
     if (M <= cfp32::kGemvMaxRows) {
@@ -261,6 +280,70 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
     }
     return launched(cfp32::launch_gemm(hi, lo, ldh, w, ldw, y, ldy, nullptr, nullptr, ldy, M, N, K,
                                        /*a_zero_padded=*/true, s, bias, nk));
+}
+
+// ---- scratch of the no-allocation entry point -------------------------------
+// One fixed array per device, in device memory that the loader provides with
+// this code object; its host-side name is only a stand-in for the symbol, so
+// host code uses the address hipGetSymbolAddress reports for the current
+// device, looked up on the first call on that device and kept.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+cfp32_status scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return CFP32_ERR_UNSUPPORTED_DEVICE;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CFP32_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cfp32_status cfp32_linear_noalloc(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,
+                                  int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if (!y || ldy < N || !extent_ok(M, ldy)) return CFP32_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!x || !w || ldx < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+    }
+    const size_t need = cfp32_linear_ex_workspace_bytes(M, N, K, CFP32_W_KN);
+    // Above 64 rows cfp32_linear splits x into planes and runs one GEMM, or
+    // splits inside the GEMM; both give the same bits.  When the planes do
+    // not fit the scratch, only the second is possible.
+    const bool fits = need == 0 || need - kAlign <= kScratchBytes;
+    if (!fits && M <= 64) return CFP32_ERR_TOO_LARGE;
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!fits) {
+        const hipError_t e = cfp32::launch_gemm_dma_split(x, ldx, w, ldw, y, ldy, M, N, K, s, nullptr, false);
+        return e == hipErrorNotSupported ? CFP32_ERR_TOO_LARGE : launched(e);
+    }
+    void *scr = nullptr;
+    st = scratch_of_current_device(&scr);
+    if (st != CFP32_OK) return st;
+    return linear_paths(x, ldx, w, ldw, false, nullptr, y, ldy, M, N, K, reinterpret_cast<uintptr_t>(scr), need, s);
 }
 
 cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y,

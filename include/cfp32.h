@@ -36,7 +36,9 @@
  * - FP16 data travels as IEEE binary16 bit patterns in uint16_t.
  * - All pointers are device memory owned by the caller.  The library never
  *   allocates, frees, synchronises or prints.  No alignment is required;
- *   kernels use wide loads only where the pointers and ld allow them.
+ *   kernels use wide loads only where the pointers and ld allow them.  The
+ *   one piece of device memory the library owns is the fixed scratch array
+ *   of cfp32_linear_noalloc (64 MiB per device, set aside by the loader).
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Calls are asynchronous and ordered on that stream.  Execution faults
  *   surface at the caller's next synchronisation.
@@ -52,7 +54,9 @@
  *   fallback).
  * - Outputs must not overlap inputs.
  * - The library keeps no mutable state besides a per-device cache of the
- *   architecture check; calls from several threads are safe.
+ *   architecture check (and cfp32_linear_noalloc's scratch array and the
+ *   cache of its address); calls from several threads are safe, except
+ *   overlapping cfp32_linear_noalloc calls on one device.
  */
 #ifndef CFP32_H
 #define CFP32_H
@@ -74,7 +78,8 @@ typedef enum {
     CFP32_OK = 0,
     CFP32_ERR_INVALID_VALUE = 1,      /* null pointer, negative size, ld too small, workspace too small, size overflow */
     CFP32_ERR_UNSUPPORTED_DEVICE = 2, /* no HIP device, or the current one is not gfx950 */
-    CFP32_ERR_HIP = 3                 /* a HIP runtime call or kernel launch failed; see cfp32_last_hip_error */
+    CFP32_ERR_HIP = 3,                /* a HIP runtime call or kernel launch failed; see cfp32_last_hip_error */
+    CFP32_ERR_TOO_LARGE = 4           /* cfp32_linear_noalloc: the problem needs more than its fixed scratch */
 } cfp32_status;
 
 /* Static, NUL-terminated description of a status code. */
@@ -177,6 +182,30 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 CFP32_API cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
                           float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* cfp32_linear without a workspace, for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation.  Arguments, results and errors are those
+ * of cfp32_linear (same paths, same kernels, the same bits), except that the
+ * scratch the kernels need (hi/lo planes, partial sums) lives in one fixed
+ * array of 64 MiB per device that the library owns: device memory set aside
+ * when the library's code is loaded on a device and held until the process
+ * ends.  This call allocates and frees nothing.
+ *   - Problems whose scratch exceeds 64 MiB return CFP32_ERR_TOO_LARGE with
+ *     nothing enqueued; above 64 rows, such problems instead run the GEMM
+ *     that splits x on the way into LDS and needs no scratch (same bits as
+ *     cfp32_linear), when x and W allow it (K % 4 == 0, ldx % 4 == 0,
+ *     ldw % 8 == 0, 16-byte aligned), else CFP32_ERR_TOO_LARGE.  cfp32_linear_
+ *     workspace_bytes(M, N, K) - 256 is the scratch a shape needs.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents; nothing in it needs to start at zero (each
+ *     kernel writes the bytes it reads first).  Calls that may overlap on
+ *     one device (different streams without an ordering between them, or
+ *     several host threads) race on the array and give wrong results: use
+ *     cfp32_linear with a workspace per stream for those.  Calls ordered on
+ *     one stream are safe. */
+CFP32_API cfp32_status cfp32_linear_noalloc(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
+                                  float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* Weight layouts for cfp32_linear_ex. */
 typedef enum {

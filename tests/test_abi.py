@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in (cf.OK, cf.ERR_INVALID_VALUE, cf.ERR_UNSUPPORTED_DEVICE, cf.ERR_HIP):
+    for s in (cf.OK, cf.ERR_INVALID_VALUE, cf.ERR_UNSUPPORTED_DEVICE, cf.ERR_HIP, cf.ERR_TOO_LARGE):
         assert cf.cfp32_status_string(s)
     assert cf.cfp32_status_string(99) == "unknown status"
 
@@ -77,6 +77,15 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
         assert need > 0
         assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, None, 0, None) == E
         assert cf.cfp32_linear(FAKE, 64, FAKE, 64, FAKE, 64, M, 64, 64, FAKE, need - 1, None) == E
+    # linear_noalloc: null pointers, short leading dimensions, negative sizes
+    assert cf.cfp32_linear_noalloc(None, 8, FAKE, 8, FAKE, 8, 2, 8, 8, None) == E
+    assert cf.cfp32_linear_noalloc(FAKE, 7, FAKE, 8, FAKE, 8, 2, 8, 8, None) == E
+    assert cf.cfp32_linear_noalloc(FAKE, 8, FAKE, 8, FAKE, 7, 2, 8, 8, None) == E
+    assert cf.cfp32_linear_noalloc(FAKE, 8, FAKE, 8, FAKE, 8, -2, 8, 8, None) == E
+    # linear_noalloc: scratch beyond its 64 MiB with at most 64 rows is
+    # refused before the device is looked at (M = 64, K = 2^20: planes of
+    # 2 x 64 x 2^20 x 2 bytes = 256 MiB)
+    assert cf.cfp32_linear_noalloc(FAKE, 1 << 20, FAKE, 8, FAKE, 8, 64, 8, 1 << 20, None) == cf.ERR_TOO_LARGE
     # linear_ex: unknown layout; [N, K] weights need ldw >= K
     assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 64, 2, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
     assert cf.cfp32_linear_ex(FAKE, 64, FAKE, 63, cf.W_NK, None, FAKE, 64, 2, 64, 64, None, 0, None) == E
@@ -169,6 +178,8 @@ def test_empty_problems_are_no_ops(lib):
     assert cf.cfp32_linear_geglu(None, 0, None, 0, None, None, 0, 3, 0, 8, None, 0, None) == cf.OK
     assert cf.cfp32_merge(None, None, 0, None, 0, 4, 0, None) == cf.OK
     assert cf.cfp32_linear(None, 0, None, 0, None, 0, 0, 8, 8, None, 0, None) == cf.OK
+    assert cf.cfp32_linear_noalloc(None, 0, None, 0, None, 0, 0, 8, 8, None) == cf.OK
+    assert cf.cfp32_linear_noalloc(None, 0, None, 0, None, 0, 5, 0, 8, None) == cf.OK
 
 
 def test_no_cpu_fallback_without_gfx950():

@@ -11,7 +11,7 @@ pointers, sizes, stream handle):
     cfp32_split, cfp32_gemm, cfp32_gemm_separate_add, cfp32_merge,
     cfp32_linear, cfp32_linear_noalloc, cfp32_linear_workspace_bytes, cfp32_linear_ex,
     cfp32_linear_ex_workspace_bytes, cfp32_linear_geglu,
-    cfp32_linear_geglu_workspace_bytes, cfp32_qkv_rotary, cfp32_status_string,
+    cfp32_linear_geglu_workspace_bytes, cfp32_linear_f32, cfp32_qkv_rotary, cfp32_status_string,
     cfp32_last_hip_error
 
 Tensor-level helpers (``split``, ``gemm``, ``merge``, ``linear``) check dtype,
@@ -44,6 +44,7 @@ EXPORTS = (
     "cfp32_linear_ex",
     "cfp32_linear_geglu_workspace_bytes",
     "cfp32_linear_geglu",
+    "cfp32_linear_f32",
     "cfp32_qkv_rotary",
 )
 
@@ -98,6 +99,8 @@ def load_library():
     lib.cfp32_linear_geglu_workspace_bytes.restype = ctypes.c_size_t
     lib.cfp32_linear_geglu.argtypes = [P, I64, P, I64, P, P, I64, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.cfp32_linear_geglu.restype = I32
+    lib.cfp32_linear_f32.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, P]
+    lib.cfp32_linear_f32.restype = I32
     lib.cfp32_qkv_rotary.argtypes = [P, I64, P, ctypes.c_double, P, P, P, I64, I64, I64, P]
     lib.cfp32_qkv_rotary.restype = I32
     _lib = lib
@@ -159,6 +162,10 @@ def cfp32_linear_geglu_workspace_bytes(M, F, K) -> int:
 def cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace, workspace_bytes, stream) -> int:
     return int(load_library().cfp32_linear_geglu(x, ldx, w, ldw, bias, out, ldo, M, F, K, workspace,
                                                  workspace_bytes, stream))
+
+
+def cfp32_linear_f32(x, ldx, w, ldw, y, ldy, M, N, K, stream) -> int:
+    return int(load_library().cfp32_linear_f32(x, ldx, w, ldw, y, ldy, M, N, K, stream))
 
 
 def cfp32_qkv_rotary(qkv, ldq, positions, theta, q, k, v, T, H, D, stream) -> int:
@@ -373,6 +380,23 @@ def linear_geglu(x, w, bias=None, out=None, workspace: Workspace | None = None, 
     pws = ws.data_ptr() if ws is not None else None
     _check(cfp32_linear_geglu(px, ldx, pw, ldw, pb, po, ldo, M, F, K, pws, need, _stream(st)),
            "cfp32_linear_geglu")
+    return out
+
+
+def linear_f32(x, w, out=None, stream=None):
+    """The true-FP32 projection y = x W: x FP32 [M, K] used as FP32, w FP16
+    [K, N] widened exactly, FP32 matrix-unit products and sums."""
+    torch = _torch()
+    px, M, K, ldx = _mat(x, (torch.float32,), "x")
+    pw, K2, N, ldw = _mat(w, _f16_dtypes(), "w")
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py, M3, N3, ldy = _mat(out, (torch.float32,), "out")
+    if (M3, N3) != (M, N):
+        raise ValueError("out has the wrong shape")
+    _check(cfp32_linear_f32(px, ldx, pw, ldw, py, ldy, M, N, K, _stream(stream)), "cfp32_linear_f32")
     return out
 
 

@@ -448,6 +448,21 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
                                        bias_up, false, true));
 }
 
+cfp32_status cfp32_linear_f32(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, void *stream)
+{
+    if (!dims_ok(M, N) || !dims_ok(K, 0)) return CFP32_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) return CFP32_OK;
+    if (!y || ldy < N || !extent_ok(M, ldy)) return CFP32_ERR_INVALID_VALUE;
+    if (K > 0) {
+        if (!x || !w || ldx < K || ldw < N) return CFP32_ERR_INVALID_VALUE;
+        if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
+    }
+    cfp32_status st = check_device();
+    if (st != CFP32_OK) return st;
+    return launched(cfp32::launch_gemm_f32(x, ldx, w, ldw, y, ldy, M, N, K, (hipStream_t)stream));
+}
+
 cfp32_status cfp32_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *positions, double theta, float *q,
                               float *k, float *v, int64_t T, int64_t H, int64_t D, void *stream)
 {

@@ -97,6 +97,11 @@ hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int
                                  int64_t ldw, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                  bool a_zero_padded, hipStream_t stream, const float *bias);
 
+// True-FP32 projection (gemm_f32.hip): y = x W with x in FP32, W widened
+// exactly to FP32, FP32 matrix-unit products and sums; any M, N, K >= 0.
+hipError_t launch_gemm_f32(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // Q/K/V packing + rotary (qkv_rotary.hip): qkv [T, >= 3HD] (ldq) -> q, k, v
 // [H][T][D]; pos (device, T entries) or null for 0 .. T-1; D even.
 hipError_t launch_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *pos, double theta, float *q, float *k,

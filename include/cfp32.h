@@ -268,6 +268,18 @@ CFP32_API cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uin
                                 const float *bias, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* True-FP32 projection (guide: true-FP32 paragraph, the build-time
+ * extension's true FP32 matrix kernels, which keep FP32 operands from being
+ * converted to FP16): the A/B partner of cfp32_linear on the same operands.
+ *   x : FP32 [M, K], ldx >= K, used as FP32 (no split, no FP16 rounding).
+ *   w : FP16 bits [K, N], ldw >= N, widened exactly to FP32.
+ *   y : FP32 [M, N], ldy >= N.
+ * FP32 products and FP32 accumulation on the matrix unit
+ * (v_mfma_f32_16x16x4_f32), a fixed summation order (repeatable bits), no
+ * workspace, one kernel launch.  Errors and empty problems as cfp32_linear. */
+CFP32_API cfp32_status cfp32_linear_f32(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
+                              float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, void *stream);
+
 /* Q/K/V packing with the rotary multiplication, one dispatch (guide: graph
  * paragraph), applied to a QKV projection's output.
  *   qkv       : FP32 [T, 3*H*D] (ldq >= 3*H*D); row t = [q | k | v], each H

@@ -3,8 +3,9 @@ the speed side is the ``fp32_ab_4096`` entry of bench.py's output).
 
 The laya.cpp Vulkan guide offers the two FP16 products as a stand-in for
 FP32 arithmetic on tensor hardware (compensated-FP32 paragraph).  Here the
-true-FP32 side is the FP32 library GEMM (torch.matmul on FP32 operands with
-TF32 off), fed the same FP32 activations and the same weights widened
+true-FP32 side is this library's own FP32 kernel (cfp32_linear_f32) and,
+for reference, the FP32 library GEMM (torch.matmul on FP32 operands with
+TF32 off), both fed the same FP32 activations and the same weights widened
 exactly from FP16.
 
 What the arithmetic fixes: hi + lo/1024 represents each activation to within
@@ -39,10 +40,15 @@ def test_compensated_error_matches_true_fp32(name):
         y_f = to_host(torch.matmul(dx, dw.float()))
     finally:
         torch.backends.cuda.matmul.allow_tf32 = prev
+    y_o = to_host(cf.linear_f32(dx, dw))
     y64, abs64 = oracle.y64(A, W)
     assert_within_tolerance(y_c, y64, abs64, f"{name} compensated")
     assert_within_tolerance(y_f, y64, abs64, f"{name} fp32 library")
+    assert_within_tolerance(y_o, y64, abs64, f"{name} fp32 own kernel")
     c_max, c_rms = rel_errors(y_c, y64, abs64)
     f_max, f_rms = rel_errors(y_f, y64, abs64)
-    note(f"{name}: compensated max {c_max:.3g} rms {c_rms:.3g}; fp32 library max {f_max:.3g} rms {f_rms:.3g}")
+    o_max, o_rms = rel_errors(y_o, y64, abs64)
+    note(f"{name}: compensated max {c_max:.3g} rms {c_rms:.3g}; fp32 library max {f_max:.3g} rms {f_rms:.3g}; "
+         f"fp32 own kernel max {o_max:.3g} rms {o_rms:.3g}")
     assert c_rms <= 4.0 * f_rms, (name, c_rms, f_rms)
+    assert c_rms <= 4.0 * o_rms, (name, c_rms, o_rms)

@@ -28,7 +28,13 @@ the FP32 library GEMM, torch.matmul with TF32 off, on the same operands),
 next to the plain projection of the same operands),
 ``separate_add_4096`` (the separate-addition accumulation mode at 4096^3,
 k_per_add 0 = plain accumulation in the same kernel configuration),
-``roofline``, ``rocprof_mfma`` (the GEMM's matrix-unit utilisation and
+``configs`` (each of the five workloads through cfp32_linear on its own:
+microseconds per call, kernel launches per call counted from a captured HIP
+graph, rates and roofline fractions, the normalised errors of y and of the
+single-FP16 product C_hi, the CPU oracle's median of 3 runs for the small
+workloads and the decode, and the FP16 library GEMM for context),
+``host`` (CPU model and cores, git revision and hashes of the sources and
+library from the build), ``roofline``, ``rocprof_mfma`` (the GEMM's matrix-unit utilisation and
 shader clock as rocprofv3 counters measured them, from the committed summary
 while the GEMM source is unchanged) and ``cpu_baseline`` (the CPU oracle
 timed on a bounded sample of the same workload on this host).
@@ -105,6 +111,199 @@ def cpu_baseline(A1, A2, W, rows_per_thread: int):
             "seconds": dt,
             "sample": f"1 decode row + {rows} of the 8192 prefill rows, K=4096, N=14336 "
                       f"(split + two FP32-accumulated products + merge, OpenMP over rows)"}
+
+
+def host_info():
+    """CPU model and usable cores, and the build the library came from."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info = {"cpu_model": model, "cpu_cores_usable": len(os.sched_getaffinity(0))}
+    lib_dir = os.path.join(ROOT, "compensated_fp32_projection_amd")
+    try:
+        with open(os.path.join(lib_dir, "build_info.json")) as f:
+            info["build"] = json.load(f)
+    except (OSError, ValueError):
+        info["build"] = None
+    h = hashlib.sha256()
+    with open(os.path.join(lib_dir, "libcfp32.so"), "rb") as f:
+        h.update(f.read())
+    info["library_sha256"] = h.hexdigest()
+    return info
+
+
+def graph_launches(fn):
+    """Kernel launches one call makes: the call is captured into a HIP graph
+    and the graph's kernel nodes are counted (None if that fails)."""
+    import ctypes
+    import torch
+    try:
+        hip = ctypes.CDLL("libamdhip64.so.7")
+        g = torch.cuda.CUDAGraph(keep_graph=True)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                fn(s.cuda_stream)
+        torch.cuda.synchronize()
+        raw = ctypes.c_void_p(g.raw_cuda_graph())
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(raw, None, ctypes.byref(n)) != 0:
+            return None
+        nodes = (ctypes.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(raw, nodes, ctypes.byref(n)) != 0:
+            return None
+        kernels = 0
+        for i in range(n.value):
+            t = ctypes.c_int(-1)
+            if hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) != 0:
+                return None
+            kernels += int(t.value == 0)  # hipGraphNodeTypeKernel
+        del g
+        return kernels
+    except Exception:
+        return None
+
+
+def timed_median(fn, stream, reps=9, min_ms=1.0):
+    """Median microseconds per call over `reps` repetitions, each a loop of n
+    calls with n chosen so that a repetition takes at least min_ms (HIP
+    events on the launch stream)."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    n = 1
+    while True:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        b.synchronize()
+        if a.elapsed_time(b) >= min_ms or n >= 1 << 14:
+            break
+        n *= 2
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b) / n * 1e3)
+    times.sort()
+    return times[len(times) // 2]
+
+
+def _cpu_median(A, W, runs):
+    """Median seconds of the oracle's compensated linear (split, two FP32
+    sums, merge) on A, W."""
+    import numpy as np
+    import oracle
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.linear_cf32(A, W)
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def _rel_err(y, y64, abs64):
+    import numpy as np
+    e = np.abs(np.asarray(y, np.float64) - y64) / np.where(abs64 > 0, abs64, 1.0)
+    return float(e.max()), float(np.sqrt(np.mean(e * e)))
+
+
+def measure_configs(stream, with_cpu: bool):
+    """Each workload through cfp32_linear on its own: microseconds per call
+    (median of timed loops of at least 1 ms), kernel launches per call,
+    FP32-equivalent TFLOP/s with the FP16-MFMA fraction (both products) or
+    GB/s with the HBM fraction (the M = 1 decode, W rotated over four copies
+    so it streams from HBM), the normalised errors of y and of the
+    single-FP16 product C_hi of the same split (the GEMM's own C_hi; the
+    oracle's for the decode, whose kernels do not expose it), the CPU
+    oracle's median of 3 runs (configs 1-3 and 5a) and the FP16 library GEMM
+    (torch.matmul on FP16 x, one product, context only)."""
+    import numpy as np
+    import torch
+
+    import compensated_fp32_projection_amd as cf
+    import oracle
+    from compensated_fp32_projection_amd import workloads
+    dev = torch.device("cuda", 0)
+    sh = stream.cuda_stream
+    pair = workloads.decode_ffn_pair()
+    cases = [("1_single_linear", workloads.single_linear().A[0], workloads.single_linear().W),
+             ("2_qkv_projection", workloads.qkv_projection().A[0], workloads.qkv_projection().W),
+             ("3_unaligned", workloads.unaligned().A[0], workloads.unaligned().W),
+             ("4_square", workloads.square().A[0], workloads.square().W),
+             ("5a_decode", pair.A[0], pair.W),
+             ("5b_ffn_prefill", pair.A[1], pair.W)]
+    del pair
+    out = {}
+    threads = oracle.num_threads()
+    for name, A, W in cases:
+        M, K = A.shape
+        N = W.shape[1]
+        x = torch.from_numpy(A).to(dev)
+        Ws = [torch.from_numpy(W.view(np.int16)).to(dev)]
+        if M == 1:  # the decode streams W from HBM: rotate copies past the 256 MB cache
+            Ws += [Ws[0].clone() for _ in range(3)]
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        need = cf.cfp32_linear_workspace_bytes(M, N, K)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def call(i, s=sh):
+            st = cf.cfp32_linear(x.data_ptr(), K, Ws[i % len(Ws)].data_ptr(), N, y.data_ptr(), N, M, N, K,
+                                 ws.data_ptr(), need, s)
+            if st != cf.OK:
+                raise RuntimeError(f"{name}: {cf.cfp32_status_string(st)}")
+
+        us = timed_median(call, stream)
+        entry = {"shape": f"{M}x{K}x{N}", "entry_point": "cfp32_linear", "us": round(us, 2),
+                 "launches": graph_launches(lambda s: call(0, s)),
+                 "tflops_fp32eq": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2),
+                 "frac_fp16_peak": round(4.0 * M * N * K / (us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4)}
+        if M == 1:
+            bytes_ = K * N * 2 + M * K * 4 + M * N * 4
+            entry["GBps"] = round(bytes_ / (us * 1e-6) / 1e9, 1)
+            entry["frac_hbm"] = round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        if M * N * K <= 4096 ** 3:  # FP64 reference of everything but the 8192-row prefill
+            call(0)
+            yh = y.cpu().numpy()
+            y64, abs64 = oracle.y64(A, W)
+            entry["e_max_y"], entry["e_rms_y"] = (float(f"{v:.3g}") for v in _rel_err(yh, y64, abs64))
+            if M > 1:
+                hi, lo = cf.split(x)
+                _, ch, _ = cf.gemm(hi, lo, Ws[0], want_y=False, want_parts=True)
+                c_hi = ch.cpu().numpy()
+                del hi, lo, ch
+            else:
+                _, c_hi, _ = oracle.linear_cf32(A, W)
+            entry["e_max_c_hi"], entry["e_rms_c_hi"] = (float(f"{v:.3g}") for v in _rel_err(c_hi, y64, abs64))
+            del y64, abs64
+        if with_cpu and M * N * K <= 1000 * 1000 * 1000:
+            t = _cpu_median(A, W, 3)
+            entry["cpu_oracle_median3_us"] = round(t * 1e6, 1)
+            entry["cpu_oracle_tflops_fp32eq"] = round(2.0 * M * N * K / t / 1e12, 5)
+            entry["cpu_oracle_threads_busy"] = min(M, threads)
+            if M == 1:
+                entry["cpu_oracle_GBps"] = round((K * N * 2 + K * 4 + N * 4) / t / 1e9, 2)
+        xh = x.half()
+        wh = Ws[0].view(torch.float16)
+        entry["fp16_library_matmul_us"] = round(timed_median(lambda i: torch.matmul(xh, wh), stream, reps=5), 2)
+        out[name] = entry
+        del x, Ws, y, ws, xh, wh
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def _read_counter_csv(path):
@@ -349,6 +548,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-per-thread", type=int, default=40)
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
@@ -525,6 +725,9 @@ def main():
     wf32 = ws.view(torch.float16).float()
     yf32 = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
     fp32_us = timed(lambda i: torch.matmul(xs, wf32, out=yf32), 20)
+    # and this library's own true-FP32 kernel (FP32 matrix unit) on the same operands
+    own_fp32_us = timed(lambda i: check(cf.cfp32_linear_f32(xs.data_ptr(), 4096, ws.data_ptr(), 4096, yf32.data_ptr(),
+                                                            4096, 4096, 4096, 4096, sh), "linear_f32"), 10)
     del lin_ws, wf32, yf32
     # The FFN projection with its GEGLU fused (x2 [8192, 4096], W [4096, 14336]
     # as gate | up, F = 7168) next to the plain projection of the same operands.
@@ -547,6 +750,8 @@ def main():
             hs.data_ptr(), ls.data_ptr(), 4096, ws.data_ptr(), 4096, ys.data_ptr(), None, None, 4096,
             4096, 4096, 4096, kpa, sh), "separate add"), 10)
     torch.cuda.synchronize()
+
+    configs = None if args.no_configs else measure_configs(stream, with_cpu=not args.no_cpu_baseline)
 
     if args.calibration_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -604,8 +809,12 @@ def main():
         "fp32_ab_4096": {
             "cfp32_linear_us": round(lin_us, 2),
             "cfp32_linear_tflops_fp32eq": round(2 * 4096 ** 3 / (lin_us * 1e-6) / 1e12, 1),
+            "fp32_own_kernel_us": round(own_fp32_us, 2),
+            "fp32_own_kernel_tflops": round(2 * 4096 ** 3 / (own_fp32_us * 1e-6) / 1e12, 1),
+            "fp32_own_kernel_frac_fp32_mfma_peak": round(2 * 4096 ** 3 / (own_fp32_us * 1e-6) / 1e12 / 157.3, 4),
             "fp32_library_matmul_us": round(fp32_us, 2),
             "fp32_library_tflops": round(2 * 4096 ** 3 / (fp32_us * 1e-6) / 1e12, 1),
+            "speedup_vs_own_fp32": round(own_fp32_us / lin_us, 2),
             "speedup": round(fp32_us / lin_us, 2),
         },
         "geglu_ffn_8192x4096x7168": {
@@ -617,9 +826,11 @@ def main():
             "gemm_us": round(sq_us, 2),
             **{f"k_per_add_{k}_us": round(v, 2) for k, v in sep_us.items()},
         },
+        "configs": configs,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "cus": props.multi_processor_count, "torch": torch.__version__,
                    "hip": getattr(torch.version, "hip", None)},
+        "host": host_info(),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -15,7 +15,10 @@ source tree.  Flags that the numerics rely on:
 from __future__ import annotations
 
 import argparse
+import datetime
 import glob
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -24,6 +27,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcfp32.so")
+# Written next to the library on every build: the git revision (and whether
+# the tree had uncommitted changes), a hash of the sources and of the
+# library, so a measurement can name the build it ran even where the source
+# tree travels without its git history.
+BUILD_INFO = os.path.join(HERE, "build_info.json")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -51,6 +59,48 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def _git(*args) -> str | None:
+    try:
+        r = subprocess.run(["git", *args], cwd=HERE, capture_output=True, text=True, timeout=20)
+        return r.stdout.strip() if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources and its public header."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(HERE, "..", "include", "cfp32.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def file_hash(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as fh:
+        for chunk in iter(lambda: fh.read(1 << 20), b""):
+            h.update(chunk)
+    return h.hexdigest()
+
+
+def write_build_info() -> dict:
+    status = _git("status", "--porcelain", "--untracked-files=no")
+    info = {
+        "git_revision": _git("rev-parse", "HEAD"),
+        "git_dirty": None if status is None else bool(status),
+        "source_sha256": source_hash(),
+        "library_sha256": file_hash(LIB),
+        "built_utc": datetime.datetime.now(datetime.timezone.utc).strftime("%Y-%m-%dT%H:%M:%SZ"),
+        "arch": ARCH,
+    }
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f, indent=1)
+    return info
+
+
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     """Compile every HIP source into libcfp32.so; returns the library path."""
     tmp = LIB + ".tmp"
@@ -68,6 +118,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     if err.strip() and (verbose or resource_usage):
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
 
 

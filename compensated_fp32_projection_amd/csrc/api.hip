@@ -84,9 +84,11 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
 
 extern "C" {
 
-const char *cfp32_status_string(cfp32_status s)
+const char *cfp32_status_string(int status)
 {
-    switch (s) {
+    // An int, not the enum: C callers may pass any value, and an out-of-range
+    // value of an enum type is not a valid C++ enum value.
+    switch (status) {
     case CFP32_OK: return "success";
     case CFP32_ERR_INVALID_VALUE: return "invalid argument (null pointer, negative size, leading dimension or workspace too small)";
     case CFP32_ERR_UNSUPPORTED_DEVICE: return "no usable device: the current HIP device is not gfx950 (there is no CPU fallback)";

@@ -503,35 +503,6 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
     return w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
 }
 
-GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
-{
-    GemmSplitPlan p{1, 0, 0};
-    // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
-    // 35-52 us; at M = 128 and 256 it measured no better than the generic
-    // kernel (75 vs 78 us, 122 vs 98 us), the partial sums costing what the
-    // wider grid gains.
-    constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kMaxRows = 64;
-    if (M <= kGemvMaxRows || M > kMaxRows || N <= 0 || K <= 0 || K % 8) return p;
-    if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
-    const int64_t tiles = ((M + kTileRows - 1) / kTileRows) * ((N + kTileCols - 1) / kTileCols);
-    if (tiles >= 128) return p;
-    int64_t c = 256 / tiles;
-    for (int64_t cc = c; cc >= 1 && cc > c - 8; --cc)
-        if ((cc * tiles) % 8 == 0) {
-            c = cc;
-            break;
-        }
-    const int64_t units = (K + kUnit - 1) / kUnit;
-    if (c > units / kMinUnits) c = units / kMinUnits;
-    // The partial sums (8 M N bytes per chunk, written and read back) stay
-    // within a quarter of W's 2 K N bytes.
-    if (c > K / (16 * M)) c = K / (16 * M);
-    if (c < 2) return p;
-    p.chunks = c;
-    p.n_pad = (N + 63) / 64 * 64;
-    p.workspace_bytes = (size_t)c * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
-    return p;
-}
 
 hipError_t launch_gemm_chunked(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                                int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,

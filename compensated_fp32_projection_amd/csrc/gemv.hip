@@ -56,10 +56,10 @@ typedef short short8_t __attribute__((ext_vector_type(8)));
 constexpr int kNoOffset = 0x7FFFFFF0;      // a raw buffer load here reads zero
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 constexpr int kStreamAux = 2;             // cache policy "nt": W is read once, do not keep it in cache
-constexpr int kTileN = 512;               // columns per tile: 1 KiB of an FP16 row
-constexpr int kTargetBlocks = 256;        // one block per CU
+constexpr int kTileN = kGemvTileN;        // columns per tile: 1 KiB of an FP16 row
+constexpr int kTargetBlocks = kGemvTargetBlocks;  // one block per CU
 constexpr int kT = 256;                   // 4 waves, 128 columns each
-constexpr int kBK = 32;                   // rows of W per stage (the MFMA's k)
+constexpr int kBK = kGemvStageRows;       // rows of W per stage (the MFMA's k)
 constexpr int kRowSlots = kTileN / 8;     // 16-byte granules per W row in LDS
 constexpr int kWSlots = kBK * kRowSlots;  // 2048 granules: 32 KiB of W per stage
 constexpr int kMaxGroups = 2;             // matrix-unit kernel: up to 2 groups of 8 rows of x
@@ -1048,32 +1048,6 @@ hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks
     return hipGetLastError();
 }
 
-GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
-{
-    GemvPlan p{};
-    if (M <= 0 || M > kGemvMaxRowsKN || N <= 0 || K <= 0) return p;
-    const int64_t ntiles = tiles_of(N);
-    if (ntiles > ((int64_t)1 << 40)) return p;  // keeps the byte count below in range
-    p.stages = (K + kBK - 1) / kBK;
-    // At most one block per CU; among those counts, the largest that deals the
-    // same number of blocks to each of the 8 XCDs (measured at 1 x 4096 x
-    // 14336: 8 chunks, 224 blocks, 0.4 us faster than 9 chunks, 252 blocks).
-    int64_t chunks = kTargetBlocks / ntiles;
-    for (int64_t c = chunks; c >= 1 && c > chunks - 8; --c)
-        if ((c * ntiles) % 8 == 0) {
-            chunks = c;
-            break;
-        }
-    if (chunks > p.stages) chunks = p.stages;
-    // Above 8 rows the partial sums (8 M N bytes per chunk, written and read
-    // back) are kept within a quarter of W's 2 K N bytes.
-    if (M > kGemvMaxRows && chunks > K / (16 * M)) chunks = K / (16 * M);
-    if (chunks < 1) chunks = 1;
-    p.chunks = chunks;
-    p.n_pad = ntiles * kTileN;
-    p.workspace_bytes = chunks == 1 ? 0 : (size_t)chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
-    return p;
-}
 
 hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                        int64_t M, int64_t N, int64_t K, float *part, size_t part_bytes, hipStream_t stream,
@@ -1107,12 +1081,6 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
 // [K, 2F] (partial sums always, even for a single chunk), then the GEGLU
 // merge.  hipErrorNotSupported (nothing enqueued) when W does not allow the
 // buffer path or `part` is missing or too small.
-GemvPlan gemv_geglu_plan(int64_t M, int64_t F, int64_t K)
-{
-    GemvPlan p = gemv_plan(M, 2 * F, K);
-    if (p.chunks > 0) p.workspace_bytes = (size_t)p.chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
-    return p;
-}
 
 hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *out, int64_t ldo,
                              int64_t M, int64_t F, int64_t K, float *part, size_t part_bytes, hipStream_t stream,

@@ -107,6 +107,13 @@ hipError_t launch_gemm_f32(const float *x, int64_t ldx, const uint16_t *w, int64
 hipError_t launch_qkv_rotary(const float *qkv, int64_t ldq, const int64_t *pos, double theta, float *q, float *k,
                              float *v, int64_t T, int64_t H, int64_t D, hipStream_t stream);
 
+// Small-M tiling shared by the planner (plans.hip) and the kernels
+// (gemv.hip): 512-column tiles (1 KiB of an FP16 row), K in stages of 32
+// rows, about one block per CU.
+constexpr int kGemvTileN = 512;
+constexpr int kGemvStageRows = 32;
+constexpr int kGemvTargetBlocks = 256;
+
 constexpr int64_t kGemvMaxRows = 8;
 // The small-M dispatches also take 8 < M <= 16 where the operands allow
 // 16-byte loads (two groups of 8 rows of x share every W fragment; [K, N]

@@ -1,0 +1,82 @@
+// Host-side planning of the K-split small-M and small-grid paths (no device
+// code): how many chunks K is cut into, and the workspace the partial sums
+// take.  Kept apart from the kernels so that the host logic -- argument
+// validation in api.hip and these plans -- can be built on its own, for
+// instance with the host sanitizers, without compiling any kernel.
+#include "launchers.h"
+
+namespace cfp32 {
+
+namespace {
+
+int64_t gemv_tiles(int64_t N) { return (N + kGemvTileN - 1) / kGemvTileN; }
+
+}  // namespace
+
+GemvPlan gemv_plan(int64_t M, int64_t N, int64_t K)
+{
+    GemvPlan p{};
+    if (M <= 0 || M > kGemvMaxRowsKN || N <= 0 || K <= 0) return p;
+    const int64_t ntiles = gemv_tiles(N);
+    if (ntiles > ((int64_t)1 << 40)) return p;  // keeps the byte count below in range
+    p.stages = (K + kGemvStageRows - 1) / kGemvStageRows;
+    // At most one block per CU; among those counts, the largest that deals the
+    // same number of blocks to each of the 8 XCDs (measured at 1 x 4096 x
+    // 14336: 8 chunks, 224 blocks, 0.4 us faster than 9 chunks, 252 blocks).
+    int64_t chunks = kGemvTargetBlocks / ntiles;
+    for (int64_t c = chunks; c >= 1 && c > chunks - 8; --c)
+        if ((c * ntiles) % 8 == 0) {
+            chunks = c;
+            break;
+        }
+    if (chunks > p.stages) chunks = p.stages;
+    // Above 8 rows the partial sums (8 M N bytes per chunk, written and read
+    // back) are kept within a quarter of W's 2 K N bytes.
+    if (M > kGemvMaxRows && chunks > K / (16 * M)) chunks = K / (16 * M);
+    if (chunks < 1) chunks = 1;
+    p.chunks = chunks;
+    p.n_pad = ntiles * kGemvTileN;
+    p.workspace_bytes = chunks == 1 ? 0 : (size_t)chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+// The GEGLU merge dispatch always follows the product dispatch, so the
+// partial sums are kept even for a single chunk.
+GemvPlan gemv_geglu_plan(int64_t M, int64_t F, int64_t K)
+{
+    GemvPlan p = gemv_plan(M, 2 * F, K);
+    if (p.chunks > 0) p.workspace_bytes = (size_t)p.chunks * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
+{
+    GemmSplitPlan p{1, 0, 0};
+    // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
+    // 35-52 us; at M = 128 and 256 it measured no better than the generic
+    // kernel (75 vs 78 us, 122 vs 98 us), the partial sums costing what the
+    // wider grid gains.
+    constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kMaxRows = 64;
+    if (M <= kGemvMaxRows || M > kMaxRows || N <= 0 || K <= 0 || K % 8) return p;
+    if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
+    const int64_t tiles = ((M + kTileRows - 1) / kTileRows) * ((N + kTileCols - 1) / kTileCols);
+    if (tiles >= 128) return p;
+    int64_t c = 256 / tiles;
+    for (int64_t cc = c; cc >= 1 && cc > c - 8; --cc)
+        if ((cc * tiles) % 8 == 0) {
+            c = cc;
+            break;
+        }
+    const int64_t units = (K + kUnit - 1) / kUnit;
+    if (c > units / kMinUnits) c = units / kMinUnits;
+    // The partial sums (8 M N bytes per chunk, written and read back) stay
+    // within a quarter of W's 2 K N bytes.
+    if (c > K / (16 * M)) c = K / (16 * M);
+    if (c < 2) return p;
+    p.chunks = c;
+    p.n_pad = (N + 63) / 64 * 64;
+    p.workspace_bytes = (size_t)c * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
+    return p;
+}
+
+}  // namespace cfp32

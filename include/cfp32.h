@@ -82,8 +82,9 @@ typedef enum {
     CFP32_ERR_TOO_LARGE = 4           /* cfp32_linear_noalloc: the problem needs more than its fixed scratch */
 } cfp32_status;
 
-/* Static, NUL-terminated description of a status code. */
-CFP32_API const char *cfp32_status_string(cfp32_status s);
+/* Static, NUL-terminated description of a status code (any int: values that
+ * are not a cfp32_status give "unknown status"). */
+CFP32_API const char *cfp32_status_string(int status);
 
 /* hipError_t value behind the last CFP32_ERR_HIP (or CFP32_ERR_UNSUPPORTED_DEVICE
  * caused by a failing device query) returned on the calling thread; 0 if none. */

@@ -59,11 +59,30 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16)
 // Eight consecutive FP16 values [col, col + 8) of one row holding `ncols`
 // valid entries, as 16 bytes; entries at or past ncols read as +0.  With
 // ALIGNED (row start and col 16-byte aligned) a full group is one 16-byte
-// load; otherwise, and at the ragged end, it is gathered element by element.
+// load.  Otherwise a full group at a 4-byte boundary is four dword loads, and
+// one 2 bytes past a boundary is five dword loads from the element before it
+// (which must be in the row, as must the element after it) joined by 16-bit
+// funnel shifts; every load is dword aligned, so none relies on the
+// hardware's unaligned-access mode (333 x 1000 x 777: 107 -> 70 us against
+// element gathers; the same five loads for both alignments, without the
+// branch, measured 80 us).  The ragged end is gathered element by element.
 template <bool ALIGNED>
 __device__ __forceinline__ uint4 load_row8(const uint16_t *__restrict__ row, int64_t col, int64_t ncols)
 {
     if (ALIGNED && col + 8 <= ncols) return *reinterpret_cast<const uint4 *>(row + col);
+    if (!ALIGNED && col + 8 <= ncols) {
+        const uint16_t *p = row + col;
+        if ((reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+            return make_uint4(q[0], q[1], q[2], q[3]);
+        }
+        if (col >= 1 && col + 9 <= ncols) {
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(p - 1);  // elements col - 1 .. col + 8
+            const uint32_t d0 = q[0], d1 = q[1], d2 = q[2], d3 = q[3], d4 = q[4];
+            return make_uint4(__builtin_amdgcn_alignbit(d1, d0, 16), __builtin_amdgcn_alignbit(d2, d1, 16),
+                              __builtin_amdgcn_alignbit(d3, d2, 16), __builtin_amdgcn_alignbit(d4, d3, 16));
+        }
+    }
     uint32_t v[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e)

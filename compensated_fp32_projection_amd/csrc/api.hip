@@ -72,9 +72,29 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Small-M path (M <= 8, and M <= 16 with [K, N] weights): the FP32
 // per-chunk partial sums (GemvPlan) from the start.  For 8 < M <= 16 the
 // size covers both, since the small-M dispatch may decline the operands.
+// [K, N] weights with N not a multiple of 8 and M > 8: after those, a
+// padded copy of W, [K, N rounded up to 8] FP16 (see linear_paths).
 int64_t split_ld(int64_t K) { return (K + 7) / 8 * 8; }
 
 size_t plane_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)split_ld(K) * 2u, kAlign); }
+
+// Bytes from the aligned base to the padded W copy: the larger of the GEMM
+// path's planes and partial sums and the small-M path's partial sums.
+// M > kGemvMaxRows, K > 0, extent_ok(M, split_ld(K)).
+size_t gemm_region_bytes(int64_t M, int64_t N, int64_t K, bool w_kn)
+{
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
+    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
+    // [K, N] with 8 < M <= 16 takes the small-M dispatches when W allows
+    // 16-byte loads, else the GEMM path: room for either.
+    const size_t small_m =
+        (w_kn && M <= cfp32::kGemvMaxRowsKN) ? round_up(cfp32::gemv_plan(M, N, K).workspace_bytes, kAlign) : 0;
+    return gemm_path > small_m ? gemm_path : small_m;
+}
+
+bool pads_w(int64_t M, int64_t N, int64_t K, bool w_kn) { return w_kn && M > cfp32::kGemvMaxRows && K > 0 && N % 8; }
+
+size_t padded_w_bytes(int64_t N, int64_t K) { return round_up((size_t)K * (size_t)split_ld(N) * 2u, kAlign); }
 
 cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, bool nk, const float *bias,
                           float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, uintptr_t base, size_t need,
@@ -176,14 +196,10 @@ size_t cfp32_linear_ex_workspace_bytes(int64_t M, int64_t N, int64_t K, int w_la
         return b == 0 ? 0 : b + kAlign;
     }
     if (!extent_ok(M, split_ld(K))) return 0;
-    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
-    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
-    // [K, N] with 8 < M <= 16 takes the small-M dispatches when W allows
-    // 16-byte loads, else the GEMM path: room for either.
-    const size_t small_m = (w_layout == CFP32_W_KN && M <= cfp32::kGemvMaxRowsKN)
-                               ? cfp32::gemv_plan(M, N, K).workspace_bytes
-                               : 0;
-    return (gemm_path > small_m ? gemm_path : small_m) + kAlign;
+    const bool w_kn = w_layout == CFP32_W_KN;
+    if (pads_w(M, N, K, w_kn) && !extent_ok(K, split_ld(N))) return 0;
+    const size_t region = gemm_region_bytes(M, N, K, w_kn);
+    return region + (pads_w(M, N, K, w_kn) ? padded_w_bytes(N, K) : 0) + kAlign;
 }
 
 size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -205,6 +221,9 @@ cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16_t *w, int
         if (!extent_ok(M, ldx) || !extent_ok(nk ? N : K, ldw)) return CFP32_ERR_INVALID_VALUE;
     }
     const size_t need = cfp32_linear_ex_workspace_bytes(M, N, K, w_layout);
+    // Above 8 rows every path with K > 0 needs a workspace; a size of 0 there
+    // means its extents would pass the 2^48-element limit.
+    if (need == 0 && M > cfp32::kGemvMaxRows && K > 0) return CFP32_ERR_INVALID_VALUE;
     if (need > 0 && (!workspace || workspace_bytes < need)) return CFP32_ERR_INVALID_VALUE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
@@ -232,6 +251,20 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
                                            bias));
     }
 
+    if (pads_w(M, N, K, !nk) && !(ldw % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0)) {
+        // W rows that do not allow 16-byte loads (N not a multiple of 8): a
+        // padded copy of W in the workspace first, one more dispatch that
+        // reads and writes W once, so that the small-M dispatches or the
+        // matrix-unit GEMM below can take it instead of the element-load
+        // kernels (333 x 1000 x 777: the projection took about 70 us with
+        // those).  The same values in the same k order: the same bits.
+        uint16_t *wp = reinterpret_cast<uint16_t *>(base + gemm_region_bytes(M, N, K, !nk));
+        const int64_t ldp = split_ld(N);
+        const hipError_t e = cfp32::launch_pad_rows(w, ldw, wp, ldp, K, N, s);
+        if (e != hipSuccess) return hip_fail(e);
+        w = wp;
+        ldw = ldp;
+    }
     if (nk && M <= cfp32::kGemvMaxRowsNK && K > 0) {
         // Up to 32 rows of x with [N, K] weights: the small-M [N, K] dispatch
         // with two or four groups of 8 rows; it enqueues nothing and returns
@@ -330,6 +363,7 @@ cfp32_status cfp32_linear_noalloc(const float *x, int64_t ldx, const uint16_t *w
         if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
     }
     const size_t need = cfp32_linear_ex_workspace_bytes(M, N, K, CFP32_W_KN);
+    if (need == 0 && M > cfp32::kGemvMaxRows && K > 0) return CFP32_ERR_INVALID_VALUE;  // as in cfp32_linear_ex
     // Above 64 rows cfp32_linear splits x into planes and runs one GEMM, or
     // splits inside the GEMM; both give the same bits.  When the planes do
     // not fit the scratch, only the second is possible.
@@ -386,6 +420,7 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
         if (!extent_ok(M, ldx) || !extent_ok(K, ldw)) return CFP32_ERR_INVALID_VALUE;
     }
     const size_t need = cfp32_linear_geglu_workspace_bytes(M, F, K);
+    if (need == 0 && M > cfp32::kGemvMaxRows && K > 0) return CFP32_ERR_INVALID_VALUE;  // as in cfp32_linear_ex
     if (need > 0 && (!workspace || workspace_bytes < need)) return CFP32_ERR_INVALID_VALUE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;

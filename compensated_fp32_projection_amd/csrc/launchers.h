@@ -16,6 +16,12 @@ hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo,
 hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
                         int64_t rows, int64_t cols, hipStream_t stream);
 
+// W [rows, cols] (ldw, any 2-byte alignment) copied into wp [rows, ldp]
+// (ldp a multiple of 8, wp 16-byte aligned), columns [cols, ldp) written as
+// +0: the form the 16-byte-load kernels take.
+hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols,
+                           hipStream_t stream);
+
 // y (ldy) and/or c_hi, c_lo (ldc) outputs; any of them may be null.
 // bias (FP32 [N], or null): every launcher that writes y adds bias[n] to the
 // merged value, as one more FP32 addition (c_hi, c_lo stay the bare products).

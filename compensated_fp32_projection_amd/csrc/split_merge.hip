@@ -53,6 +53,24 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const float *__restrict
     }
 }
 
+// Rows of FP16 W copied to rows of ldp (a multiple of 8) elements, columns
+// [cols, ldp) zero: one thread per 8 columns of a row, each writing one
+// 16-byte piece; the source may sit at any 2-byte offset (load_row8 reads
+// it in dwords, or element by element at the row's end).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads) void pad_rows_kernel(const uint16_t *__restrict__ w, int64_t ldw,
+                                                            uint16_t *__restrict__ wp, int64_t ldp, int64_t rows,
+                                                            int64_t cols)
+{
+    const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+    if (c >= ldp) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const uint4 v = load_row8<false>(w + r * ldw, c, cols);
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(wp + r * ldp + c));
+    }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const float *__restrict__ c_hi,
                                                          const float *__restrict__ c_lo, int64_t ldc,
@@ -101,6 +119,15 @@ hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo,
         split_kernel<false><<<grid_for(rows, cols_out, 1), kThreads, 0, stream>>>(x, ldx, hi, lo, ldh, rows, cols,
                                                                                    cols_out);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols,
+                           hipStream_t stream)
+{
+    if (ldp % 8 || ldp < cols || !aligned(wp, 16)) return hipErrorInvalidValue;
+    if ((ldp / 8 + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    pad_rows_kernel<<<grid_for(rows, ldp, 8), kThreads, 0, stream>>>(w, ldw, wp, ldp, rows, cols);
     return hipGetLastError();
 }
 

@@ -150,7 +150,10 @@ CFP32_API cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t
  * at most 256 chunks (1 MiB for M = 1, N = 14336, K = 4096).
  * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes, plus, for
  * M <= 64 on small grids, FP32 partial sums of split K (at most a quarter
- * of W's bytes); for M <= 16 at least the small-M partial sums. */
+ * of W's bytes); for M <= 16 at least the small-M partial sums.  M > 8
+ * with N not a multiple of 8: also a padded copy of W, 2 * K * N8 bytes
+ * (N8 = N rounded up to 8).  Returns 0 too when these sizes would pass
+ * 2^48 elements; cfp32_linear then refuses the shape. */
 CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* The whole projection y = x W (guide: compensated-FP32 paragraph; small
@@ -169,6 +172,10 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         kernel instead, which leaves the workspace untouched.
  * 8 < M <= 16 with W 16-byte aligned and ldw % 8 == 0: the same two
  *         launches, two groups of 8 rows of x sharing every W fragment.
+ * M  > 8 with N not a multiple of 8 and W rows that do not allow 16-byte
+ *         loads: one more launch first copies W into the workspace with
+ *         rows of N8 elements (columns past N zero); the paths below then
+ *         run on that copy as on a 16-byte-aligned W (the same bits).
  * M  > 8 otherwise: cfp32_split into the workspace, then cfp32_gemm with
  *         the merged epilogue (two launches); or, for N <= 4096 with at
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,

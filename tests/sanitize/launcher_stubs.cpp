@@ -27,6 +27,11 @@ hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float
     reached("launch_merge");
 }
 
+hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols, hipStream_t stream)
+{
+    reached("launch_pad_rows");
+}
+
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w, int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc, int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream, const float *bias, bool w_nk, bool geglu_rmw)
 {
     reached("launch_gemm");

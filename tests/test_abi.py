@@ -134,7 +134,7 @@ def test_workspace_sizes(lib):
         assert cf.cfp32_linear_ex_workspace_bytes(*shape, cf.W_KN) == cf.cfp32_linear_workspace_bytes(*shape)
     assert cf.cfp32_linear_ex_workspace_bytes(1, 14336, 4096, cf.W_NK) == 0
     assert cf.cfp32_linear_ex_workspace_bytes(8, 4096, 4096, cf.W_NK) == 0
-    assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, cf.W_NK) == 2 * 256 + 256
+    assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, cf.W_NK) == 2 * 256 + 256  # no W copy for [N, K]
     assert cf.cfp32_linear_ex_workspace_bytes(9, 5, 1, 7) == 0
     # cfp32_linear_geglu: M <= 8 holds partial sums for all 2F columns, even
     # for a single chunk; M > 8 the hi/lo planes, and up to 16 rows at least
@@ -147,8 +147,11 @@ def test_workspace_sizes(lib):
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(-1, 10, 10) == 0
-    # two FP16 planes of M x roundup(K, 8), 256-byte aligned, plus alignment slack
-    assert cf.cfp32_linear_workspace_bytes(9, 5, 1) == 2 * 256 + 256
+    # two FP16 planes of M x roundup(K, 8), 256-byte aligned, plus alignment
+    # slack; N not a multiple of 8: then a padded copy of W, K x roundup(N, 8)
+    # FP16 (here 1 x 8), 256-byte aligned
+    assert cf.cfp32_linear_workspace_bytes(9, 5, 1) == 2 * 256 + 256 + 256
+    assert cf.cfp32_linear_workspace_bytes(9, 8, 1) == 2 * 256 + 256
     assert cf.cfp32_linear_workspace_bytes(4096, 4096, 4096) == 2 * 4096 * 4096 * 2 + 256
     # M > 8 with fewer than 128 output tiles of 128 x 256 and K % 8 == 0: K is
     # split (chunks x tiles about 256, a multiple of 8 where within reach, at
@@ -162,8 +165,11 @@ def test_workspace_sizes(lib):
     # the partial-sum bytes: 6 chunks, N rounded up to 576.
     planes = 2 * ((40 * 4104 * 2 + 255) // 256 * 256)
     assert cf.cfp32_linear_workspace_bytes(40, 520, 4104) == planes + 6 * 40 * 2 * 576 * 4 + 256
-    # M > 64, K % 8 != 0, K too short for two chunks, or enough tiles: planes only.
-    assert cf.cfp32_linear_workspace_bytes(300, 777, 1000) == 2 * ((300 * 1000 * 2 + 255) // 256 * 256) + 256
+    # M > 64, K % 8 != 0, K too short for two chunks, or enough tiles: planes
+    # only (and the padded W copy, 1000 x 784 FP16, when N % 8 != 0).
+    assert cf.cfp32_linear_workspace_bytes(300, 777, 1000) == \
+        2 * ((300 * 1000 * 2 + 255) // 256 * 256) + 1000 * 784 * 2 + 256
+    assert cf.cfp32_linear_workspace_bytes(300, 776, 1000) == 2 * ((300 * 1000 * 2 + 255) // 256 * 256) + 256
     assert cf.cfp32_linear_workspace_bytes(64, 14336, 4100) == 2 * ((64 * 4104 * 2 + 255) // 256 * 256) + 256
     assert cf.cfp32_linear_workspace_bytes(64, 14336, 256) == 2 * 64 * 256 * 2 + 256
     assert cf.cfp32_linear_workspace_bytes(512, 14336, 4096) == 2 * 512 * 4096 * 2 + 256

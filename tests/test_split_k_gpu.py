@@ -68,14 +68,22 @@ def test_split_k_against_reference_and_across_kernels(M, K, N):
     from 17 ([K, N]) or 33 ([N, K]) rows up (LDS-DMA kernel with the hi and
     lo rows stacked into one tile), cut K at the same places: the same bits,
     within tolerance.  Below that aligned weights take the small-M
-    dispatches (checked against the reference)."""
+    dispatches (checked against the reference).  [K, N] weights with N not a
+    multiple of 8 are copied into aligned rows first, so up to 16 rows they
+    too take the small-M dispatches."""
     need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
     assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
     A, W = workloads.random_case(M * 7 + K + N, M, K, N, a_scale=20.0)
     note(f"split-K {M}x{K}x{N}")
-    y = run(A, W, w_offset=1)
+    y = run(A, W, layout=cf.W_NK, w_offset=1)  # generic kernel, split K
     check(y, A, W, f"split-K {M}x{K}x{N}")
-    runs = [run(A, W, layout=cf.W_NK, w_offset=1)]
+    y_kn = run(A, W, w_offset=1)
+    runs = []
+    if M > 16 or N % 8 == 0:  # the [K, N] run cuts K the same way
+        runs.append(y_kn)
+    else:
+        check(y_kn, A, W, f"small-M (padded W) {M}x{K}x{N}")
+        assert np.array_equal(y_kn.view(np.uint32), run(A, W).view(np.uint32))
     if M > 16:
         runs.append(run(A, W))
     if M > 32:
@@ -85,7 +93,7 @@ def test_split_k_against_reference_and_across_kernels(M, K, N):
     for y2 in runs:
         assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
     y3 = run(A, W, w_offset=1)
-    assert np.array_equal(y.view(np.uint32), y3.view(np.uint32)), "not deterministic"
+    assert np.array_equal(y_kn.view(np.uint32), y3.view(np.uint32)), "not deterministic"
 
 
 # (M, K, N): ragged M inside the second group of 8 rows, ragged N and K, the

@@ -286,13 +286,17 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s, bias));
 
-    // One launch with the split inside the GEMM, where that is faster than the
-    // split kernel plus the GEMM (measured on MI355X: N <= 4096 with at least
-    // 128 output tiles of 128 x 256; for wider N each block's share of the
-    // split, repeated once per 256 columns, outweighs the separate pass, and
-    // small grids are latency-bound).  Both ways multiply the same operands in
-    // the same order, so the results are identical.
-    if (N <= 4096 && ((M + 127) / 128) * ((N + 255) / 256) >= 128) {
+    // One launch with the split inside the GEMM (launch_gemm_dma_split: the
+    // operands and k order of the two-launch path, so the same bits) for
+    // narrow W: N <= 1024 with at least 128 output tiles of 128 x 256.
+    // There the separate split pass is large against the GEMM and saving it
+    // pays (8192 x 1024 x 768: 38 vs 54 us; 32768 x 4096 x 512: 327 vs
+    // 416 us; 16384 x 4096 x 1024: 304 vs 322 us).  From N = 1536 on, the
+    // conversion each block repeats per 256 columns lengthens every stage's
+    // memory phase more than the pass costs (4096 x 4096 x 1536: 130 vs
+    // 121 us; 4096^3: 297 vs 253 us; interleaved runs under sustained load
+    // on MI355X).
+    if (N <= 1024 && ((M + 127) / 128) * ((N + 255) / 256) >= 128) {
         const hipError_t e = cfp32::launch_gemm_dma_split(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
         if (e != hipErrorNotSupported) return launched(e);
     }

@@ -177,7 +177,7 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         rows of N8 elements (columns past N zero); the paths below then
  *         run on that copy as on a 16-byte-aligned W (the same bits).
  * M  > 8 otherwise: cfp32_split into the workspace, then cfp32_gemm with
- *         the merged epilogue (two launches); or, for N <= 4096 with at
+ *         the merged epilogue (two launches); or, for N <= 1024 with at
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
  *         ldw % 8 == 0, x and w 16-byte aligned, one GEMM launch that splits
  *         x on the way into LDS (the workspace is then not touched; both give

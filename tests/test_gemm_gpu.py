@@ -331,14 +331,14 @@ def test_linear_tensor_helper():
     assert_within_tolerance(to_host(y), y64, abs64, "helper")
 
 
-@pytest.mark.parametrize("M,K,N", [(8200, 1000, 504), (4096, 4096, 4096), (16384, 256, 296), (8200, 1001, 504),
-                                   (8200, 1000, 500)])
+@pytest.mark.parametrize("M,K,N", [(8200, 1000, 504), (4096, 4096, 1024), (16384, 256, 296), (8200, 1001, 504),
+                                   (8200, 1000, 500), (4096, 4096, 4096)])
 def test_linear_fused_split_matches_two_launches(M, K, N):
-    """Shapes for which cfp32_linear splits x inside the GEMM (N <= 4096, at
+    """Shapes for which cfp32_linear splits x inside the GEMM (N <= 1024, at
     least 128 output tiles, K % 4 == 0, ldw % 8 == 0): identical bits to
     cfp32_split + cfp32_gemm, and within tolerance of the FP64 reference.
-    K = 1001 (partial 16-byte granules of x) and N = ldw = 500 take the
-    two-launch path instead."""
+    K = 1001 (partial 16-byte granules of x), N = ldw = 500 and N = 4096
+    take the two-launch path instead."""
     A, W = workloads.random_case(M + K + N, M, K, N, a_scale=30.0)
     note(f"linear fused split {M}x{K}x{N}")
     y = run_linear(A, W)

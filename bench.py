@@ -229,8 +229,10 @@ def measure_configs(stream, with_cpu: bool):
     so it streams from HBM), the normalised errors of y and of the
     single-FP16 product C_hi of the same split (the GEMM's own C_hi; the
     oracle's for the decode, whose kernels do not expose it), the CPU
-    oracle's median of 3 runs (configs 1-3 and 5a) and the FP16 library GEMM
-    (torch.matmul on FP16 x, one product, context only)."""
+    oracle's median of 3 runs (configs 1-3 and 5a; one run for config 4),
+    the FP64 reference's time (for information), the SHA-256 of the input
+    arrays (the same bytes the oracle and the GPU receive) and the FP16
+    library GEMM (torch.matmul on FP16 x, one product, context only)."""
     import numpy as np
     import torch
 
@@ -267,7 +269,10 @@ def measure_configs(stream, with_cpu: bool):
                 raise RuntimeError(f"{name}: {cf.cfp32_status_string(st)}")
 
         us = timed_median(call, stream)
-        entry = {"shape": f"{M}x{K}x{N}", "entry_point": "cfp32_linear", "us": round(us, 2),
+        entry = {"shape": f"{M}x{K}x{N}", "entry_point": "cfp32_linear",
+                 "sha256_A": hashlib.sha256(np.ascontiguousarray(A).tobytes()).hexdigest()[:16],
+                 "sha256_W": hashlib.sha256(np.ascontiguousarray(W).tobytes()).hexdigest()[:16],
+                 "us": round(us, 2),
                  "launches": graph_launches(lambda s: call(0, s)),
                  "tflops_fp32eq": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2),
                  "frac_fp16_peak": round(4.0 * M * N * K / (us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4)}
@@ -278,7 +283,9 @@ def measure_configs(stream, with_cpu: bool):
         if M * N * K <= 4096 ** 3:  # FP64 reference of everything but the 8192-row prefill
             call(0)
             yh = y.cpu().numpy()
+            t0 = time.perf_counter()
             y64, abs64 = oracle.y64(A, W)
+            entry["cpu_fp64_reference_us"] = round((time.perf_counter() - t0) * 1e6, 1)
             entry["e_max_y"], entry["e_rms_y"] = (float(f"{v:.3g}") for v in _rel_err(yh, y64, abs64))
             if M > 1:
                 hi, lo = cf.split(x)
@@ -289,9 +296,10 @@ def measure_configs(stream, with_cpu: bool):
                 _, c_hi, _ = oracle.linear_cf32(A, W)
             entry["e_max_c_hi"], entry["e_rms_c_hi"] = (float(f"{v:.3g}") for v in _rel_err(c_hi, y64, abs64))
             del y64, abs64
-        if with_cpu and M * N * K <= 1000 * 1000 * 1000:
-            t = _cpu_median(A, W, 3)
-            entry["cpu_oracle_median3_us"] = round(t * 1e6, 1)
+        if with_cpu and M * N * K <= 4096 ** 3:
+            runs = 3 if M * N * K <= 1000 * 1000 * 1000 else 1
+            t = _cpu_median(A, W, runs)
+            entry["cpu_oracle_median3_us" if runs == 3 else "cpu_oracle_once_us"] = round(t * 1e6, 1)
             entry["cpu_oracle_tflops_fp32eq"] = round(2.0 * M * N * K / t / 1e12, 5)
             entry["cpu_oracle_threads_busy"] = min(M, threads)
             if M == 1:

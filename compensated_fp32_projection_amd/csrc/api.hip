@@ -92,6 +92,25 @@ size_t gemm_region_bytes(int64_t M, int64_t N, int64_t K, bool w_kn)
     return gemm_path > small_m ? gemm_path : small_m;
 }
 
+// Largest grid of the in-block split-K kernel (see linear_paths).
+constexpr int64_t kKsplitMaxBlocks = 512;
+
+// GEGLU (M > kGemvMaxRows): as cfp32_linear_ex over the [K, 2F] weight, the
+// GEMM path (planes, plus split-K partial sums on small grids), or up to 16
+// rows the small-M dispatches when W allows 16-byte loads; then, for F % 8
+// != 0, a padded copy of W for the small-grid kernel: gate columns at 0, up
+// columns at F rounded up to 8, [K, 2 F8] FP16.
+size_t geglu_region_bytes(int64_t M, int64_t F, int64_t K)
+{
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, 2 * F, K);
+    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
+    const size_t small_m =
+        M <= cfp32::kGemvMaxRowsKN ? round_up(cfp32::gemv_geglu_plan(M, F, K).workspace_bytes, kAlign) : 0;
+    return gemm_path > small_m ? gemm_path : small_m;
+}
+
+size_t geglu_padded_w_bytes(int64_t F, int64_t K) { return round_up((size_t)K * (size_t)split_ld(F) * 4u, kAlign); }
+
 bool pads_w(int64_t M, int64_t N, int64_t K, bool w_kn) { return w_kn && M > cfp32::kGemvMaxRows && K > 0 && N % 8; }
 
 size_t padded_w_bytes(int64_t N, int64_t K) { return round_up((size_t)K * (size_t)split_ld(N) * 2u, kAlign); }
@@ -260,7 +279,7 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         // those).  The same values in the same k order: the same bits.
         uint16_t *wp = reinterpret_cast<uint16_t *>(base + gemm_region_bytes(M, N, K, !nk));
         const int64_t ldp = split_ld(N);
-        const hipError_t e = cfp32::launch_pad_rows(w, ldw, wp, ldp, K, N, s);
+        const hipError_t e = cfp32::launch_pad_rows(w, ldw, wp, ldp, K, N, ldp, s);
         if (e != hipSuccess) return hip_fail(e);
         w = wp;
         ldw = ldp;
@@ -288,6 +307,17 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s, bias));
 
+    // Small grids that do not split K across blocks: one launch of the kernel
+    // that splits K across the four waves of each 32 x 64 tile and x in
+    // registers, while its grid fits the GPU at once (two blocks per CU:
+    // 512).  333 x 1000 x 777: 30 -> 18 us; 96 x 4096 x 4096: 62 -> 29 us;
+    // 256 x 4096 x 4096: 71 -> 47-55 us; 1024^3: 26 -> 20 us.  Beyond 512
+    // blocks the 32 x 64 tiles re-read x and W more than the large-tile
+    // kernels (512 x 768 x 2304: 21 -> 23 us, 512 x 4096 x 4096: 81 -> 90 us).
+    if (cfp32::gemm_split_plan(M, N, K).chunks <= 1 && cfp32::ksplit_blocks(M, N) <= kKsplitMaxBlocks) {
+        const hipError_t e = cfp32::launch_gemm_ksplit(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     // One launch with the split inside the GEMM (launch_gemm_dma_split: the
     // operands and k order of the two-launch path, so the same bits) for
     // narrow W: N <= 1024 with at least 128 output tiles of 128 x 256.
@@ -405,13 +435,8 @@ size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_t K)
         return b == 0 ? 0 : b + kAlign;
     }
     if (!extent_ok(M, split_ld(K))) return 0;
-    // As cfp32_linear_ex over the [K, 2F] weight: the GEMM path (planes, plus
-    // split-K partial sums on small grids), or up to 16 rows the small-M
-    // dispatches when W allows 16-byte loads.
-    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, 2 * F, K);
-    const size_t gemm_path = 2 * plane_bytes(M, K) + (sp.chunks > 1 ? round_up(sp.workspace_bytes, kAlign) : 0);
-    const size_t small_m = M <= cfp32::kGemvMaxRowsKN ? cfp32::gemv_geglu_plan(M, F, K).workspace_bytes : 0;
-    return (gemm_path > small_m ? gemm_path : small_m) + kAlign;
+    if (F % 8 && !extent_ok(K, 2 * split_ld(F))) return 0;
+    return geglu_region_bytes(M, F, K) + (F % 8 ? geglu_padded_w_bytes(F, K) : 0) + kAlign;
 }
 
 cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, const float *bias,
@@ -463,6 +488,39 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
         if (e != hipSuccess) return hip_fail(e);
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F,
                                            0, false, s, bias_up, false, true));
+    }
+
+    // Small grids: the small-grid kernel with the GEGLU epilogue exactly where
+    // cfp32_linear_ex takes the small-grid kernel for the [K, 2F] projection
+    // (W 16-byte loadable, or copied because 2F % 8 != 0), so that every gate
+    // and up sum is that projection's.  The kernel needs the up columns
+    // 16-byte aligned: for F % 8 != 0 it runs on a copy of W with the up
+    // columns moved to F rounded up to 8 (the same values in the same order).
+    // (Up to 16 rows cfp32_linear_ex takes the small-M dispatches first, as
+    // the branch above does.)
+    if (M > cfp32::kGemvMaxRowsKN && cfp32::gemm_split_plan(M, 2 * F, K).chunks <= 1 &&
+        cfp32::ksplit_blocks(M, 2 * F) <= kKsplitMaxBlocks) {
+        const bool w16 = ldw % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+        // Whether cfp32_linear_ex takes the small-grid kernel: on W itself, or,
+        // when 2F % 8 != 0, on its compact copy (rows of 2F rounded up to 8 at
+        // a 256-byte aligned address, which `base` stands in for here).
+        const bool linear_ksplit =
+            w16 ? cfp32::ksplit_supported(x, ldx, w, ldw, M, 2 * F, K, false)
+                : (2 * F) % 8 != 0 && cfp32::ksplit_supported(x, ldx, reinterpret_cast<const void *>(base),
+                                                              split_ld(2 * F), M, 2 * F, K, false);
+        if (linear_ksplit && w16 && F % 8 == 0) {
+            const hipError_t e = cfp32::launch_gemm_ksplit_geglu(x, ldx, w, ldw, F, out, ldo, M, F, K, s, bias);
+            if (e != hipErrorNotSupported) return launched(e);
+        } else if (linear_ksplit) {  // F % 8 != 0: the copy with the up columns at F8
+            uint16_t *wp = reinterpret_cast<uint16_t *>(base + geglu_region_bytes(M, F, K));
+            const int64_t f8 = split_ld(F);
+            hipError_t e = cfp32::launch_pad_rows(w, ldw, wp, 2 * f8, K, F, f8, s);
+            if (e != hipSuccess) return hip_fail(e);
+            e = cfp32::launch_pad_rows(w + F, ldw, wp + f8, 2 * f8, K, F, f8, s);
+            if (e != hipSuccess) return hip_fail(e);
+            e = cfp32::launch_gemm_ksplit_geglu(x, ldx, wp, 2 * f8, f8, out, ldo, M, F, K, s, bias);
+            if (e != hipErrorNotSupported) return launched(e);
+        }
     }
 
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);

@@ -16,11 +16,33 @@ hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo,
 hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float *y, int64_t ldy,
                         int64_t rows, int64_t cols, hipStream_t stream);
 
-// W [rows, cols] (ldw, any 2-byte alignment) copied into wp [rows, ldp]
-// (ldp a multiple of 8, wp 16-byte aligned), columns [cols, ldp) written as
-// +0: the form the 16-byte-load kernels take.
+// Small-grid projection in one launch (gemm_ksplit.hip): FP32 x split in
+// registers, K split across the block's four waves, fixed-order reduction,
+// merge (+ bias) into y; W [K, N], or [N, K] with w_nk.  hipErrorNotSupported
+// (nothing enqueued) unless K % 8 == 0, ldx % 4 == 0, ldw % 8 == 0, x and w
+// 16-byte aligned and the byte offsets fit 31 bits.  ksplit_blocks: its
+// grid (one block per 32 x 64 output tile).
+constexpr int kKsplitTileM = 32, kKsplitTileN = 64;
+hipError_t launch_gemm_ksplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias, bool w_nk);
+int64_t ksplit_blocks(int64_t M, int64_t N);  // plans.hip
+// Whether launch_gemm_ksplit takes these operands (plans.hip).
+bool ksplit_supported(const void *x, int64_t ldx, const void *w, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                      bool w_nk);
+// The same kernel with the GEGLU epilogue: out [M, F] = gelu(x W_gate +
+// b_gate) * (x W_up + b_up), W [K, >= up_off + F] with the gate columns at
+// 0 and the up columns at up_off (a multiple of 8, >= F), bias [2F] (gate |
+// up) or null.  hipErrorNotSupported as launch_gemm_ksplit.
+hipError_t launch_gemm_ksplit_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int64_t up_off,
+                                    float *out, int64_t ldo, int64_t M, int64_t F, int64_t K, hipStream_t stream,
+                                    const float *bias);
+
+// W [rows, cols] (ldw, any 2-byte alignment) copied into the first cols_out
+// columns of wp [rows, ldp] (ldp and cols_out multiples of 8, wp 16-byte
+// aligned), columns [cols, cols_out) written as +0: the form the
+// 16-byte-load kernels take.
 hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols,
-                           hipStream_t stream);
+                           int64_t cols_out, hipStream_t stream);
 
 // y (ldy) and/or c_hi, c_lo (ldc) outputs; any of them may be null.
 // bias (FP32 [N], or null): every launcher that writes y adds bias[n] to the

@@ -79,4 +79,23 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     return p;
 }
 
+int64_t ksplit_blocks(int64_t M, int64_t N)
+{
+    return ((M + kKsplitTileM - 1) / kKsplitTileM) * ((N + kKsplitTileN - 1) / kKsplitTileN);
+}
+
+bool ksplit_supported(const void *x, int64_t ldx, const void *w, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                      bool w_nk)
+{
+    // Byte offsets the kernel forms (buffer loads: 31 bits, with room for
+    // the stages it loads past K and a tile's overhang) stay below this.
+    constexpr int64_t kLimit = 0x7FFFFFF0 - (1 << 20);
+    if (M <= 0 || N <= 0 || K <= 0 || K % 8 || ldx % 4 || ldw % 8) return false;
+    if (((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w)) & 15) != 0) return false;
+    if (M > kLimit || N > kLimit || K > kLimit) return false;
+    if ((M + kKsplitTileM) * ldx * 4 + (K + 1024) * 4 >= kLimit) return false;
+    const int64_t w_bytes = w_nk ? (N + kKsplitTileN) * ldw * 2 + (K + 1024) * 2 : (K + 1024) * ldw * 2;
+    return w_bytes < kLimit && N + kKsplitTileN < ((int64_t)1 << 31);
+}
+
 }  // namespace cfp32

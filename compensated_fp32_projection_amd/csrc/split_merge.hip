@@ -53,18 +53,19 @@ __global__ __launch_bounds__(kThreads) void split_kernel(const float *__restrict
     }
 }
 
-// Rows of FP16 W copied to rows of ldp (a multiple of 8) elements, columns
-// [cols, ldp) zero: one thread per 8 columns of a row, each writing one
-// 16-byte piece; the source may sit at any 2-byte offset (load_row8 reads
-// it in dwords, or element by element at the row's end).
+// Rows of FP16 W copied to rows of ldp elements, the first cols_out of
+// each written (columns [cols, cols_out) zero; cols_out and ldp multiples
+// of 8): one thread per 8 columns of a row, each writing one 16-byte piece;
+// the source may sit at any 2-byte offset (load_row8 reads it in dwords, or
+// element by element at the row's end).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void pad_rows_kernel(const uint16_t *__restrict__ w, int64_t ldw,
                                                             uint16_t *__restrict__ wp, int64_t ldp, int64_t rows,
-                                                            int64_t cols)
+                                                            int64_t cols, int64_t cols_out)
 {
     const int64_t c = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
-    if (c >= ldp) return;
+    if (c >= cols_out) return;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
         const uint4 v = load_row8<false>(w + r * ldw, c, cols);
         __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(wp + r * ldp + c));
@@ -123,11 +124,11 @@ hipError_t launch_split(const float *x, int64_t ldx, uint16_t *hi, uint16_t *lo,
 }
 
 hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols,
-                           hipStream_t stream)
+                           int64_t cols_out, hipStream_t stream)
 {
-    if (ldp % 8 || ldp < cols || !aligned(wp, 16)) return hipErrorInvalidValue;
-    if ((ldp / 8 + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    pad_rows_kernel<<<grid_for(rows, ldp, 8), kThreads, 0, stream>>>(w, ldw, wp, ldp, rows, cols);
+    if (ldp % 8 || cols_out % 8 || cols_out < cols || cols_out > ldp || !aligned(wp, 16)) return hipErrorInvalidValue;
+    if ((cols_out / 8 + kThreads - 1) / kThreads > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    pad_rows_kernel<<<grid_for(rows, cols_out, 8), kThreads, 0, stream>>>(w, ldw, wp, ldp, rows, cols, cols_out);
     return hipGetLastError();
 }
 

@@ -176,6 +176,12 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         loads: one more launch first copies W into the workspace with
  *         rows of N8 elements (columns past N zero); the paths below then
  *         run on that copy as on a 16-byte-aligned W (the same bits).
+ * M  > 8, small grids (at most 512 output tiles of 32 x 64, K not split
+ *         across blocks as below) with K % 8 == 0, ldx % 4 == 0 and x, W
+ *         16-byte loadable: one launch that splits x in registers and splits
+ *         K across the four waves of each tile, the partial tiles summed in a
+ *         fixed order (its own repeatable bits; the same for [K, N] and
+ *         [N, K] weights).
  * M  > 8 otherwise: cfp32_split into the workspace, then cfp32_gemm with
  *         the merged epilogue (two launches); or, for N <= 1024 with at
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
@@ -248,7 +254,10 @@ CFP32_API cfp32_status cfp32_linear_ex(const float *x, int64_t ldx, const uint16
                              const float *bias, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes cfp32_linear_geglu needs (0 when none is needed). */
+/* Workspace bytes cfp32_linear_geglu needs (0 when none is needed): as
+ * cfp32_linear's for the [K, 2F] projection, and for M > 8 with F % 8 != 0
+ * also room for a copy of W with rows of 2 F8 elements (F8 = F rounded up
+ * to 8). */
 CFP32_API size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_t K);
 
 /* The feed-forward projection with its GEGLU fused (guide: graph paragraph,
@@ -269,9 +278,13 @@ CFP32_API size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_
  * (M <= 16 with 16-byte aligned W, ldw % 8 == 0): the small-M product
  * dispatch over all 2F columns, then a merge dispatch that forms out.
  * M <= 64 on small grids with K % 8 == 0: the split, a GEMM over chunks of K
- * into FP32 partial sums in the workspace, then that merge dispatch.  Other
- * cases run the gate projection into out and the up projection with a
- * read-modify-write epilogue (one more launch). */
+ * into FP32 partial sums in the workspace, then that merge dispatch.
+ * M > 16 where cfp32_linear_ex takes its one-launch small-grid kernel for
+ * the [K, 2F] projection: that kernel with the GEGLU in its epilogue (for
+ * F % 8 != 0 after two launches that copy W into the workspace with the up
+ * columns at F rounded up to 8).  Other cases run the gate projection into
+ * out and the up projection with a read-modify-write epilogue (one more
+ * launch). */
 CFP32_API cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
                                 const float *bias, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K,
                                 void *workspace, size_t workspace_bytes, void *stream);

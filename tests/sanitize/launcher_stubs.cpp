@@ -27,7 +27,7 @@ hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float
     reached("launch_merge");
 }
 
-hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols, hipStream_t stream)
+hipError_t launch_pad_rows(const uint16_t *w, int64_t ldw, uint16_t *wp, int64_t ldp, int64_t rows, int64_t cols, int64_t cols_out, hipStream_t stream)
 {
     reached("launch_pad_rows");
 }
@@ -95,6 +95,17 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
 hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K, float *part, size_t part_bytes, hipStream_t stream, const float *bias)
 {
     reached("launch_gemv_geglu");
+}
+
+
+hipError_t launch_gemm_ksplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias, bool w_nk)
+{
+    reached("launch_gemm_ksplit");
+}
+
+hipError_t launch_gemm_ksplit_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int64_t up_off, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K, hipStream_t stream, const float *bias)
+{
+    reached("launch_gemm_ksplit_geglu");
 }
 
 }  // namespace cfp32

@@ -141,8 +141,11 @@ def test_workspace_sizes(lib):
     # those partial sums (the small-M dispatches when W allows 16-byte loads).
     assert cf.cfp32_linear_geglu_workspace_bytes(1, 7168, 4096) == 8 * 1 * 2 * 14336 * 4 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 8) == 1 * 2 * 2 * 512 * 4 + 256
-    assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 1 * 9 * 2 * 512 * 4 + 256
-    assert cf.cfp32_linear_geglu_workspace_bytes(17, 5, 1) == 2 * 512 + 256  # planes of 17 x 8 FP16
+    # F % 8 != 0 above 8 rows: then a padded copy of W for the small-grid
+    # kernel, K x 2 roundup(F, 8) FP16 (here 1 x 16), 256-byte aligned.
+    assert cf.cfp32_linear_geglu_workspace_bytes(9, 5, 1) == 1 * 9 * 2 * 512 * 4 + 256 + 256
+    assert cf.cfp32_linear_geglu_workspace_bytes(17, 5, 1) == 2 * 512 + 256 + 256  # planes of 17 x 8 FP16
+    assert cf.cfp32_linear_geglu_workspace_bytes(17, 8, 1) == 2 * 512 + 256
     assert cf.cfp32_linear_geglu_workspace_bytes(2, 16, 0) == 0
     assert cf.cfp32_linear_workspace_bytes(0, 10, 10) == 0
     assert cf.cfp32_linear_workspace_bytes(100, 10, 0) == 0

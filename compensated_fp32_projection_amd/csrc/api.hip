@@ -92,8 +92,32 @@ size_t gemm_region_bytes(int64_t M, int64_t N, int64_t K, bool w_kn)
     return gemm_path > small_m ? gemm_path : small_m;
 }
 
-// Largest grid of the in-block split-K kernel (see linear_paths).
+// Largest grid of the in-block split-K kernel (see ksplit_route).
 constexpr int64_t kKsplitMaxBlocks = 512;
+
+// Whether the projection takes the small-grid kernel (gemm_ksplit.hip) when
+// its operands allow it; M > kGemvMaxRows, K > 0.  Its grid must fit the
+// GPU at once (two blocks per CU: at most 512 blocks).
+//  * [K, N] weights, up to 16 rows: where the small-M dispatches would run
+//    a grid of fewer than 64 blocks and K <= 1024 (at most 8 stages per
+//    wave).  16 x 256 x 384: 11.5 -> 7.2 us; 12 x 256 x 2048: 11.5 -> 7.3
+//    us; 16 x 1024 x 1024: 13.9 -> 10.2 us; with K = 4096 (32 stages per
+//    wave) it lost (16 x 4096 x 1024: 16.4 -> 20.5 us).
+//  * [N, K] weights up to 32 rows: never (the small-M [N, K] dispatch).
+//  * Above: where K is not split across blocks.  96 x 4096 x 4096: 62 ->
+//    27 us; 256 x 4096 x 4096: 72 -> 46 us; 1024^3: 26 -> 21 us; beyond 512
+//    blocks its 32 x 64 tiles re-read x and W more than the large tiles do
+//    (512 x 768 x 2304: 21 -> 23 us; 512 x 4096 x 4096: 81 -> 90 us).
+bool ksplit_route(int64_t M, int64_t N, int64_t K, bool nk)
+{
+    if (cfp32::ksplit_blocks(M, N) > kKsplitMaxBlocks) return false;
+    if (nk && M <= cfp32::kGemvMaxRowsNK) return false;
+    if (!nk && M <= cfp32::kGemvMaxRowsKN) {
+        const cfp32::GemvPlan p = cfp32::gemv_plan(M, N, K);
+        return K <= 1024 && p.chunks * ((N + cfp32::kGemvTileN - 1) / cfp32::kGemvTileN) < 64;
+    }
+    return cfp32::gemm_split_plan(M, N, K).chunks <= 1;
+}
 
 // GEGLU (M > kGemvMaxRows): as cfp32_linear_ex over the [K, 2F] weight, the
 // GEMM path (planes, plus split-K partial sums on small grids), or up to 16
@@ -284,6 +308,14 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         w = wp;
         ldw = ldp;
     }
+    if (K > 0 && ksplit_route(M, N, K, nk)) {
+        // The small-grid kernel: one launch, x split in registers, K split
+        // across the four waves of each 32 x 64 tile (see ksplit_route); it
+        // enqueues nothing and returns hipErrorNotSupported when x or W do
+        // not allow its 16-byte loads.
+        const hipError_t e = cfp32::launch_gemm_ksplit(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     if (nk && M <= cfp32::kGemvMaxRowsNK && K > 0) {
         // Up to 32 rows of x with [N, K] weights: the small-M [N, K] dispatch
         // with two or four groups of 8 rows; it enqueues nothing and returns
@@ -307,17 +339,6 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, y, ldy, nullptr, nullptr, ldy, M,
                                            N, 0, false, s, bias));
 
-    // Small grids that do not split K across blocks: one launch of the kernel
-    // that splits K across the four waves of each 32 x 64 tile and x in
-    // registers, while its grid fits the GPU at once (two blocks per CU:
-    // 512).  333 x 1000 x 777: 30 -> 18 us; 96 x 4096 x 4096: 62 -> 29 us;
-    // 256 x 4096 x 4096: 71 -> 47-55 us; 1024^3: 26 -> 20 us.  Beyond 512
-    // blocks the 32 x 64 tiles re-read x and W more than the large-tile
-    // kernels (512 x 768 x 2304: 21 -> 23 us, 512 x 4096 x 4096: 81 -> 90 us).
-    if (cfp32::gemm_split_plan(M, N, K).chunks <= 1 && cfp32::ksplit_blocks(M, N) <= kKsplitMaxBlocks) {
-        const hipError_t e = cfp32::launch_gemm_ksplit(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
-        if (e != hipErrorNotSupported) return launched(e);
-    }
     // One launch with the split inside the GEMM (launch_gemm_dma_split: the
     // operands and k order of the two-launch path, so the same bits) for
     // narrow W: N <= 1024 with at least 128 output tiles of 128 x 256.
@@ -474,32 +495,13 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
         return launched(cfp32::launch_gemv(x, ldx, w_up, ldw, out, ldo, M, F, K, nullptr, 0, s, bias_up, true));
     }
 
-    if (M <= cfp32::kGemvMaxRowsKN && K > 0) {
-        // Up to 16 rows: the small-M product dispatch over all 2F columns and
-        // the GEGLU merge, when W allows 16-byte loads (else the GEMM path).
-        const hipError_t e = cfp32::launch_gemv_geglu(x, ldx, w, ldw, out, ldo, M, F, K,
-                                                      reinterpret_cast<float *>(base), need - kAlign, s, bias);
-        if (e != hipErrorNotSupported) return launched(e);
-    }
-
-    if (K == 0) {
-        hipError_t e = cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F, 0,
-                                          false, s, bias);
-        if (e != hipSuccess) return hip_fail(e);
-        return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F,
-                                           0, false, s, bias_up, false, true));
-    }
-
     // Small grids: the small-grid kernel with the GEGLU epilogue exactly where
     // cfp32_linear_ex takes the small-grid kernel for the [K, 2F] projection
     // (W 16-byte loadable, or copied because 2F % 8 != 0), so that every gate
     // and up sum is that projection's.  The kernel needs the up columns
     // 16-byte aligned: for F % 8 != 0 it runs on a copy of W with the up
     // columns moved to F rounded up to 8 (the same values in the same order).
-    // (Up to 16 rows cfp32_linear_ex takes the small-M dispatches first, as
-    // the branch above does.)
-    if (M > cfp32::kGemvMaxRowsKN && cfp32::gemm_split_plan(M, 2 * F, K).chunks <= 1 &&
-        cfp32::ksplit_blocks(M, 2 * F) <= kKsplitMaxBlocks) {
+    if (M > cfp32::kGemvMaxRows && K > 0 && ksplit_route(M, 2 * F, K, false)) {
         const bool w16 = ldw % 8 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
         // Whether cfp32_linear_ex takes the small-grid kernel: on W itself, or,
         // when 2F % 8 != 0, on its compact copy (rows of 2F rounded up to 8 at
@@ -521,6 +523,22 @@ cfp32_status cfp32_linear_geglu(const float *x, int64_t ldx, const uint16_t *w, 
             e = cfp32::launch_gemm_ksplit_geglu(x, ldx, wp, 2 * f8, f8, out, ldo, M, F, K, s, bias);
             if (e != hipErrorNotSupported) return launched(e);
         }
+    }
+
+    if (M <= cfp32::kGemvMaxRowsKN && K > 0) {
+        // Up to 16 rows: the small-M product dispatch over all 2F columns and
+        // the GEGLU merge, when W allows 16-byte loads (else the GEMM path).
+        const hipError_t e = cfp32::launch_gemv_geglu(x, ldx, w, ldw, out, ldo, M, F, K,
+                                                      reinterpret_cast<float *>(base), need - kAlign, s, bias);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
+
+    if (K == 0) {
+        hipError_t e = cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F, 0,
+                                          false, s, bias);
+        if (e != hipSuccess) return hip_fail(e);
+        return launched(cfp32::launch_gemm(nullptr, nullptr, 0, nullptr, 0, out, ldo, nullptr, nullptr, ldo, M, F,
+                                           0, false, s, bias_up, false, true));
     }
 
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);

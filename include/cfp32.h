@@ -176,12 +176,14 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         loads: one more launch first copies W into the workspace with
  *         rows of N8 elements (columns past N zero); the paths below then
  *         run on that copy as on a 16-byte-aligned W (the same bits).
- * M  > 8, small grids (at most 512 output tiles of 32 x 64, K not split
- *         across blocks as below) with K % 8 == 0, ldx % 4 == 0 and x, W
- *         16-byte loadable: one launch that splits x in registers and splits
- *         K across the four waves of each tile, the partial tiles summed in a
- *         fixed order (its own repeatable bits; the same for [K, N] and
- *         [N, K] weights).
+ * M  > 8, small grids (at most 512 output tiles of 32 x 64; above 16 rows
+ *         ([K, N]) or 32 rows ([N, K]) where K is not split across blocks
+ *         as below; from 9 to 16 rows with [K, N] weights where K <= 1024 and
+ *         the small-M dispatches would run fewer than 64 blocks) with
+ *         K % 8 == 0, ldx % 4 == 0 and x, W 16-byte loadable: one launch that
+ *         splits x in registers and splits K across the four waves of each
+ *         tile, the partial tiles summed in a fixed order (its own repeatable
+ *         bits; the same for [K, N] and [N, K] weights).
  * M  > 8 otherwise: cfp32_split into the workspace, then cfp32_gemm with
  *         the merged epilogue (two launches); or, for N <= 1024 with at
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
@@ -279,7 +281,7 @@ CFP32_API size_t cfp32_linear_geglu_workspace_bytes(int64_t M, int64_t F, int64_
  * dispatch over all 2F columns, then a merge dispatch that forms out.
  * M <= 64 on small grids with K % 8 == 0: the split, a GEMM over chunks of K
  * into FP32 partial sums in the workspace, then that merge dispatch.
- * M > 16 where cfp32_linear_ex takes its one-launch small-grid kernel for
+ * M > 8 where cfp32_linear_ex takes its one-launch small-grid kernel for
  * the [K, 2F] projection: that kernel with the GEGLU in its epilogue (for
  * F % 8 != 0 after two launches that copy W into the workspace with the up
  * columns at F rounded up to 8).  Other cases run the gate projection into

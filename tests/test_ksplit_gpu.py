@@ -84,6 +84,28 @@ def test_ksplit_against_reference(M, K, N):
         assert np.array_equal(y.view(np.uint32), y_nk.view(np.uint32)), "[N, K] and [K, N] differ"
 
 
+# (M, K, N): up to 16 rows the kernel replaces the small-M dispatches on
+# tiny grids with K <= 1024: the single-linear workload's shape, a wider W,
+# two groups of rows, a K that is not a whole number of stages, odd N.
+TINY = [(16, 256, 384), (12, 256, 2048), (9, 512, 512), (16, 1024, 1024), (13, 264, 200), (10, 96, 77)]
+
+
+@pytest.mark.parametrize("M,K,N", TINY)
+def test_small_rows_on_tiny_grids(M, K, N):
+    A, W = workloads.random_case(M * 17 + K + N, M, K, N, a_scale=40.0)
+    note(f"tiny grid {M}x{K}x{N}")
+    y, _ = run(A, W)
+    y64, abs64 = oracle.y64(A, W)
+    assert_within_tolerance(y, y64, abs64, f"tiny {M}x{K}x{N}")
+    _, ch, _ = oracle.linear_cf32(A, W)
+    assert_better_than_single(y, ch, y64, abs64, f"tiny {M}x{K}x{N}")
+    y2, _ = run(A, W)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not deterministic"
+    bias = np.random.default_rng(M).standard_normal(N).astype(np.float32)
+    yb, _ = run(A, W, bias=bias)
+    assert np.array_equal(yb.view(np.uint32), (y + bias[None, :]).astype(np.float32).view(np.uint32))
+
+
 def test_ksplit_unaligned_workload_with_padded_copy():
     """The unaligned workload (333 x 1000 x 777): W is first copied into rows
     of 784 elements, then the small-grid kernel runs (two launches)."""
@@ -133,8 +155,8 @@ def test_ksplit_wider_grids_keep_the_tiled_kernels():
 # (M, K, F): F % 8 == 0 (the kernel reads W in place); F % 8 == 4 (2F % 8
 # == 0: cfp32_linear_ex runs the kernel on W in place, the GEGLU entry on a
 # copy with the up columns moved to F rounded up to 8); F odd (2F % 8 != 0:
-# both run on copies of W).
-GEGLU = [(70, 520, 96), (40, 256, 300), (100, 1000, 77)]
+# both run on copies of W); 12 rows on a tiny grid.
+GEGLU = [(70, 520, 96), (40, 256, 300), (100, 1000, 77), (12, 256, 300)]
 
 
 @pytest.mark.parametrize("with_bias", [False, True])

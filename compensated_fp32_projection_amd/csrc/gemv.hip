@@ -762,8 +762,11 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 #pragma unroll
         for (int j = 0; j < kNkLoads; ++j) {
             const int base = (s & 1) ? w_base[1][j] : w_base[0][j];
-            const int o = (s < nst && base >= 0 && kNkPiece * p + w_k[j] < (int)K) ? base + 2 * kNkPiece * p
-                                                                                    : kNoOffset;
+            // Bitwise conditions, no short circuit: a branch around a load
+            // leaves the compiler unsure how many loads are in flight, and it
+            // then waits for all of them.
+            const int o = ((s < nst) & (base >= 0) & (kNkPiece * p + w_k[j] < (int)K)) ? base + 2 * kNkPiece * p
+                                                                                      : kNoOffset;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (CFP32_LDS void *)(buf + 64 * (kNkLoads * wave + j)), 16,
                                                      o, 0, 0, kStreamAux);
         }
@@ -782,7 +785,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     // ONE: lane l of the wave loads x[0][512 p + 64 wave + l] into slot p % 2.
     auto load_x1 = [&](auto slot_tag, int p) __attribute__((always_inline)) {
         const int k = kNkPiece * p + 32 * kNkSteps * wave + lane;
-        const int o = p < pieces && k < (int)K ? 4 * k : kNoOffset;
+        const int o = (p < pieces) & (k < (int)K) ? 4 * k : kNoOffset;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(nk_xslot<decltype(slot_tag)::value>() + 16 * wave),
                                                  4, o, 0, 0, 0);
     };
@@ -792,11 +795,11 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 #pragma unroll
             for (int t = 0; t < kNkSteps; ++t) {
                 const int k = kNkPiece * p + 32 * (kNkSteps * wave + t);
-                const bool ok = x_base[q] >= 0 && p < pieces && k + 8 * kq < (int)K;
-                xs[q][t][0] = __builtin_bit_cast(
-                    floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k : kNoOffset, 0, 0));
-                xs[q][t][1] = __builtin_bit_cast(
-                    floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, ok ? x_base[q] + 4 * k + 16 : kNoOffset, 0, 0));
+                const bool ok = (x_base[q] >= 0) & (p < pieces) & (k + 8 * kq < (int)K);
+                const int o = ok ? x_base[q] + 4 * k : kNoOffset;
+                const int o2 = ok ? x_base[q] + 4 * k + 16 : kNoOffset;
+                xs[q][t][0] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, o, 0, 0));
+                xs[q][t][1] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_x, o2, 0, 0));
             }
     };
     half8_t af[G][kNkSteps];
@@ -883,13 +886,19 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     issue(std::integral_constant<int, 2>{}, 2);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * kNkLoads));  // x of piece 0 and stage 0 landed
     block_barrier();
-    for (int s = 0; s < nst; s += 4) {  // nst is even
+    // Whole rounds of four stages, then the last pair (nst is even).  A
+    // branch inside the loop body made the compiler wait for every load in
+    // flight at the head of each round (one vmcnt(1) per round).
+    const int nr = nst / 4 * 4;
+    for (int s = 0; s < nr; s += 4) {
         stage(std::integral_constant<int, 0>{}, s);
         stage(std::integral_constant<int, 1>{}, s + 1);
-        if (s + 2 < nst) {
-            stage(std::integral_constant<int, 2>{}, s + 2);
-            stage(std::integral_constant<int, 3>{}, s + 3);
-        }
+        stage(std::integral_constant<int, 2>{}, s + 2);
+        stage(std::integral_constant<int, 3>{}, s + 3);
+    }
+    if (nr < nst) {
+        stage(std::integral_constant<int, 0>{}, nr);
+        stage(std::integral_constant<int, 1>{}, nr + 1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the trailing zero loads, before the ring is reused
     if constexpr (!ONE) {

@@ -358,21 +358,29 @@ __global__ __launch_bounds__(kValuThreads) void gemv_valu_kernel(GemvArgs g)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
 
-    for (int64_t kb = r0 + wave; kb < r1; kb += (int64_t)WV * kValuU) {
-        uint4 wv[kValuU];
+    // Rows past r1 load zeros (W) and read x as 0 through selects, not
+    // branches: a branch around a load (the x row test) made the compiler
+    // wait for every load in flight at the join (M = 2: 24.9 -> 23.8 us).
+    // Their products are +0 and leave the sums' bits unchanged (a sum that
+    // starts at +0 never becomes -0).  A second set of rows in flight
+    // (double-buffered registers) ran slower at M = 1 (23.0 -> 23.6 us).
+    const int64_t step = (int64_t)WV * kValuU;
+    auto load = [&](uint4 (&wv)[kValuU], float (&xv)[kValuU][MR], int64_t kb) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kValuU; ++u) {
             const int64_t k = kb + (int64_t)u * WV;
-            const int off = (k < r1 && n < g.N) ? (int)((k * g.ldw + n) * 2) : kNoOffset;
+            const bool in = k < r1;
+            const int off = (in & (n < g.N)) ? (int)((k * g.ldw + n) * 2) : kNoOffset;
             wv[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, off, 0, kStreamAux));
-        }
-        float xv[kValuU][MR];
+            const int64_t kc = in ? k : r1 - 1;  // a row inside x, read and then replaced by 0
 #pragma unroll
-        for (int u = 0; u < kValuU; ++u) {
-            const int64_t k = kb + (int64_t)u * WV;
-#pragma unroll
-            for (int m = 0; m < MR; ++m) xv[u][m] = (k < r1) ? g.x[m * g.ldx + k] : 0.0f;
+            for (int m = 0; m < MR; ++m) {
+                const float v = g.x[m * g.ldx + kc];
+                xv[u][m] = in ? v : 0.0f;
+            }
         }
+    };
+    auto compute = [&](const uint4 (&wv)[kValuU], const float (&xv)[kValuU][MR]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < kValuU; ++u) {
             const uint32_t d[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
@@ -391,6 +399,12 @@ __global__ __launch_bounds__(kValuThreads) void gemv_valu_kernel(GemvArgs g)
                 }
             }
         }
+    };
+    for (int64_t kb = r0 + wave; kb < r1; kb += step) {
+        uint4 wv[kValuU];
+        float xv[kValuU][MR];
+        load(wv, xv, kb);
+        compute(wv, xv);
     }
 
 #pragma unroll
@@ -785,7 +799,7 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
     // ONE: lane l of the wave loads x[0][512 p + 64 wave + l] into slot p % 2.
     auto load_x1 = [&](auto slot_tag, int p) __attribute__((always_inline)) {
         const int k = kNkPiece * p + 32 * kNkSteps * wave + lane;
-        const int o = (p < pieces) & (k < (int)K) ? 4 * k : kNoOffset;
+        const int o = ((p < pieces) & (k < (int)K)) ? 4 * k : kNoOffset;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_x, (CFP32_LDS void *)(nk_xslot<decltype(slot_tag)::value>() + 16 * wave),
                                                  4, o, 0, 0, 0);
     };

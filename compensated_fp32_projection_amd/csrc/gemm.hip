@@ -30,6 +30,8 @@
 //   * Out-of-range rows, columns and k read as zero and are not stored, so
 //     any M, N, K >= 1 works.  16-byte global loads are used when the base
 //     pointer and leading dimension allow it, element loads otherwise.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 #include "tile_order.h"
@@ -125,7 +127,7 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 // WNK: W is given as [N, K] (ldw >= K); its 16-byte k-granules are loaded and
 // stored exactly like those of A, no transpose needed.
 template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0, bool WNK = false>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM <= 32 && SEP == 0 ? 2 : 1))) void gemm_kernel(GemmArgs g)
 {
     static_assert(SEP == 0 || SEP == 1 || SEP % 4 == 0, "separate additions per MFMA or per whole stages");
     __shared__ uint4 lds[2 * T::LDS_STAGE];
@@ -185,8 +187,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             }
     };
 
-    uint4 ra[2][T::A_CHUNKS];
-    uint4 rw[T::W_ITERS][8];
+    // Staging registers.  The 32 x 128 tile (plain accumulation, 16-byte
+    // loads) keeps two sets, so that a stage's loads land in one set while
+    // the previous stage's set is written to LDS; the others use set 0 only.
+    constexpr bool kTwoSets = BUF && T::BM <= 32 && SEP == 0;
+    uint4 ra_set[2][2][T::A_CHUNKS];
+    uint4 rw_set[2][T::W_ITERS][8];
 
     // Buffer-load state (used only when BUF): wave-uniform descriptors and
     // per-thread byte offsets that do not change from stage to stage; the
@@ -221,35 +227,47 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
             const int b = tid + kThreads * j;
             const int kgw = b / (T::BN / 8), nc = b % (T::BN / 8);
             const int64_t gn = n0 + 8 * nc;
-            voff_w[j] = gn < g.N ? (int)((8 * kgw * g.ldw + gn) * 2) : kNoOffset;
+            voff_w[j] = gn < g.N && b < T::W_BLOCKS ? (int)((8 * kgw * g.ldw + gn) * 2) : kNoOffset;
         }
     }
 
-    auto load_stage_buf = [&](int64_t k0) {
+    // The scalar offsets are wave-uniform; readfirstlane states so, which
+    // keeps the compiler from wrapping each load in a loop over the distinct
+    // values of an offset it could not prove uniform.
+    auto load_stage_buf = [&](auto set_tag, int64_t k0) {
+        auto &ra = ra_set[decltype(set_tag)::value];
+        auto &rw = rw_set[decltype(set_tag)::value];
+        const int so_k = __builtin_amdgcn_readfirstlane((int)(k0 * 2));
 #pragma unroll
         for (int i = 0; i < T::A_CHUNKS; ++i) {
-            ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], (int)(k0 * 2), 0));
-            ra[1][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, voff_a[i], (int)(k0 * 2), 0));
+            ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], so_k, 0));
+            ra[1][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, voff_a[i], so_k, 0));
         }
         if constexpr (WNK) {
 #pragma unroll
             for (int q = 0; q < T::W_NK_CHUNKS; ++q)
                 rw[q >> 3][q & 7] =
-                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_wn[q], (int)(k0 * 2), 0));
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_wn[q], so_k, 0));
             return;
         }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
-            if (tid + kThreads * j < T::W_BLOCKS) {
+            // With two register sets, threads past the stage's W blocks load
+            // too (offsets no buffer reaches, values never stored), so every
+            // wave issues the same loads and the compiler's wait counts
+            // between the sets stay exact; otherwise they skip the loads.
+            if (!kTwoSets && tid + kThreads * j >= T::W_BLOCKS) continue;
 #pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    rw[j][r] = __builtin_bit_cast(
-                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[j], (int)((k0 + r) * g.ldw * 2), 0));
+            for (int r = 0; r < 8; ++r) {
+                const int so_w = __builtin_amdgcn_readfirstlane((int)((k0 + r) * g.ldw * 2));
+                rw[j][r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[j], so_w, 0));
             }
         }
     };
 
-    auto load_stage = [&](int64_t k0) {
+    auto load_stage = [&](auto set_tag, int64_t k0) {
+        auto &ra = ra_set[decltype(set_tag)::value];
+        auto &rw = rw_set[decltype(set_tag)::value];
 #pragma unroll
         for (int i = 0; i < T::A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
@@ -287,7 +305,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         }
     };
 
-    auto store_stage = [&](int st) {
+    auto store_stage = [&](auto set_tag, int st) {
+        auto &ra = ra_set[decltype(set_tag)::value];
+        auto &rw = rw_set[decltype(set_tag)::value];
         uint4 *s = lds + st * T::LDS_STAGE;
 #pragma unroll
         for (int i = 0; i < T::A_CHUNKS; ++i) {
@@ -374,34 +394,75 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g)
         }
     };
 
-    // K loop.  Stage kt is multiplied out of LDS buffer kt&1 while stage kt+1
-    // is fetched into registers; one barrier per stage.  Full stages use the
-    // buffer loads, so the main loop has no branch; the ragged last stage (if
-    // K is not a multiple of 64) is peeled off and uses guarded loads.
-    // (Chunk boundaries are multiples of 64, so only the chunk that ends at K
-    // can have a ragged last stage.)
+    // K loop.  Stage kt is multiplied out of LDS buffer kt & 1; its
+    // successors travel in the two register sets.  Full stages use the
+    // buffer loads, so the main loops have no branch; the ragged last stage
+    // (if K is not a multiple of 64) uses guarded loads.  (Chunk boundaries
+    // are multiples of 64, so only the chunk that ends at K can have a
+    // ragged last stage.)
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
     const int64_t nk = u_end - u_begin;
     const int64_t nk_full = BUF ? (klim - k_begin) / kBK : 0;
     if (nk == 0) {
         // K == 0: nothing to accumulate; the epilogue writes +0.
+    } else if (kTwoSets && nk_full >= 4) {
+        // Two stages ahead: while stage kt is multiplied, stage kt + 1 waits
+        // in one register set to be written to LDS and stage kt + 2 loads
+        // into the other, so two memory round trips overlap each stage's
+        // MFMAs.  Invariant at the top of a pair (kt even): LDS buffer 0
+        // holds stage kt, set 1 holds (or is loading) stage kt + 1.
+        load_stage_buf(S0{}, k_begin);
+        load_stage_buf(S1{}, k_begin + kBK);
+        store_stage(S0{}, 0);
+        __syncthreads();
+        int64_t kt = 0;
+        for (; kt + 3 < nk_full; kt += 2) {
+            load_stage_buf(S0{}, k_begin + (kt + 2) * kBK);
+            compute_stage(0, kt);
+            store_stage(S1{}, 1);
+            __syncthreads();
+            load_stage_buf(S1{}, k_begin + (kt + 3) * kBK);
+            compute_stage(1, kt + 1);
+            store_stage(S0{}, 0);
+            __syncthreads();
+        }
+        // 2 to 4 stages remain (kt + 1 < nk_full, kt + 3 >= nk_full >= nk - 1):
+        // the same steps with guarded loads, which also cover a ragged last
+        // stage.
+        for (; kt + 1 < nk; ++kt) {
+            const bool more = kt + 2 < nk;
+            if ((kt & 1) == 0) {
+                if (more) load_stage(S0{}, k_begin + (kt + 2) * kBK);
+                compute_stage(0, kt);
+                store_stage(S1{}, 1);
+            } else {
+                if (more) load_stage(S1{}, k_begin + (kt + 2) * kBK);
+                compute_stage(1, kt);
+                store_stage(S0{}, 0);
+            }
+            __syncthreads();
+        }
+        compute_stage((int)(kt & 1), kt);
     } else {
+        // Short or unaligned K: one stage ahead.
         if (nk_full > 0)
-            load_stage_buf(k_begin);
+            load_stage_buf(S0{}, k_begin);
         else
-            load_stage(k_begin);
-        store_stage(0);
+            load_stage(S0{}, k_begin);
+        store_stage(S0{}, 0);
         __syncthreads();
         int64_t kt = 0;
         for (; kt + 1 < nk_full; ++kt) {
-            load_stage_buf(k_begin + (kt + 1) * kBK);
+            load_stage_buf(S0{}, k_begin + (kt + 1) * kBK);
             compute_stage((int)(kt & 1), kt);
-            store_stage((int)((kt + 1) & 1));
+            store_stage(S0{}, (int)((kt + 1) & 1));
             __syncthreads();
         }
         for (; kt + 1 < nk; ++kt) {
-            load_stage(k_begin + (kt + 1) * kBK);
+            load_stage(S0{}, k_begin + (kt + 1) * kBK);
             compute_stage((int)(kt & 1), kt);
-            store_stage((int)((kt + 1) & 1));
+            store_stage(S0{}, (int)((kt + 1) & 1));
             __syncthreads();
         }
         compute_stage((int)(kt & 1), kt);

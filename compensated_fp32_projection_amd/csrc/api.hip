@@ -354,6 +354,15 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
         if (e != hipErrorNotSupported) return launched(e);
     }
 
+    // Grids too small for the GPU: K split into chunks (partial sums after the
+    // planes in the workspace) and a merge dispatch.  Otherwise, on grids of
+    // the generic kernel's 32 x 128 tile, the split happens in its registers
+    // (one launch, the bits of the two below).
+    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
+    if (sp.chunks <= 1) {
+        const hipError_t e = cfp32::launch_gemm_xsplit(x, ldx, w, ldw, y, ldy, M, N, K, s, bias, nk);
+        if (e != hipErrorNotSupported) return launched(e);
+    }
     uint16_t *hi = reinterpret_cast<uint16_t *>(base);
     uint16_t *lo = reinterpret_cast<uint16_t *>(base + plane_bytes(M, K));
     const int64_t ldh = split_ld(K);
@@ -361,9 +370,6 @@ cfp32_status linear_paths(const float *x, int64_t ldx, const uint16_t *w, int64_
     // read whole 16-byte groups past K.
     hipError_t e = cfp32::launch_split(x, ldx, hi, lo, ldh, M, K, ldh, s);
     if (e != hipSuccess) return hip_fail(e);
-    // Grids too small for the GPU: K split into chunks (partial sums after the
-    // planes in the workspace) and a merge dispatch.
-    const cfp32::GemmSplitPlan sp = cfp32::gemm_split_plan(M, N, K);
     if (sp.chunks > 1) {
         float *part = reinterpret_cast<float *>(base + 2 * plane_bytes(M, K));
         e = cfp32::launch_gemm_chunked(hi, lo, ldh, w, ldw, y, ldy, M, N, K, /*a_zero_padded=*/true, s, bias, nk,

@@ -126,7 +126,15 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
 //
 // WNK: W is given as [N, K] (ldw >= K); its 16-byte k-granules are loaded and
 // stored exactly like those of A, no transpose needed.
-template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0, bool WNK = false>
+//
+// XF: A is the FP32 input x itself (a_hi holds x, lda its row stride in
+// elements; a_lo unused), and the split happens in registers (split_value,
+// the conversion of the split dispatch): the eight values of a k-group
+// arrive as two 16-byte loads into the two staging slots that otherwise hold
+// the hi and lo granules, and are written to LDS as those granules.  The
+// planes are the split dispatch's, so every bit of the result is that of
+// split + GEMM.  Only the 32 x 128 tile with 16-byte loads takes it.
+template <class T, bool AL_A, bool AL_W, bool BUF, int SEP = 0, bool WNK = false, bool XF = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM <= 32 && SEP == 0 ? 2 : 1))) void gemm_kernel(GemmArgs g)
 {
     static_assert(SEP == 0 || SEP == 1 || SEP % 4 == 0, "separate additions per MFMA or per whole stages");
@@ -191,16 +199,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
     // loads) keeps two sets, so that a stage's loads land in one set while
     // the previous stage's set is written to LDS; the others use set 0 only.
     constexpr bool kTwoSets = BUF && T::BM <= 32 && SEP == 0;
+    static_assert(!XF || kTwoSets, "the FP32-input form is the 32 x 128 tile's");
+    const float *xf = reinterpret_cast<const float *>(g.a_hi);  // XF: x
     uint4 ra_set[2][2][T::A_CHUNKS];
     uint4 rw_set[2][T::W_ITERS][8];
 
     // Buffer-load state (used only when BUF): wave-uniform descriptors and
     // per-thread byte offsets that do not change from stage to stage; the
     // stage's k offset travels in the scalar offset.
-    const __amdgpu_buffer_rsrc_t rs_hi =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_hi), 0, (int)(g.M * g.lda * 2), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rs_lo =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.a_lo), 0, (int)(g.M * g.lda * 2), kBufferWord3);
+    constexpr int kAElem = XF ? 4 : 2;  // bytes per A element in memory
+    const __amdgpu_buffer_rsrc_t rs_hi = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(g.a_hi), 0, (int)(g.M * g.lda * kAElem), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs_lo = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(XF ? g.a_hi : g.a_lo), 0, (int)(g.M * g.lda * kAElem), kBufferWord3);
     const __amdgpu_buffer_rsrc_t rs_w =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(g.w), 0, (int)((WNK ? g.N : g.K) * g.ldw * 2),
                                           kBufferWord3);
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
         for (int i = 0; i < T::A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
             const int64_t gm = m0 + (c >> 3);
-            voff_a[i] = gm < g.M ? (int)((gm * g.lda + 8 * (c & 7)) * 2) : kNoOffset;
+            voff_a[i] = gm < g.M ? (int)((gm * g.lda + 8 * (c & 7)) * kAElem) : kNoOffset;
         }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
@@ -240,6 +251,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
         const int so_k = __builtin_amdgcn_readfirstlane((int)(k0 * 2));
 #pragma unroll
         for (int i = 0; i < T::A_CHUNKS; ++i) {
+            if constexpr (XF) {  // x[k .. k + 3] and x[k + 4 .. k + 7]
+                const int so_x = __builtin_amdgcn_readfirstlane((int)(k0 * 4));
+                ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], so_x, 0));
+                ra[1][i] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i] + 16, so_x, 0));
+                continue;
+            }
             ra[0][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_hi, voff_a[i], so_k, 0));
             ra[1][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_lo, voff_a[i], so_k, 0));
         }
@@ -273,6 +291,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             const int c = tid + kThreads * i;
             const int kg = c & 7, row = c >> 3;
             const int64_t gm = m0 + row, gk = k0 + 8 * kg;
+            if constexpr (XF) {  // ragged stage: values past klim (or rows past M) read as +0
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = gm < g.M && gk + e < klim ? xf[gm * g.lda + gk + e] : 0.0f;
+                ra[0][i] = make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                                      __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3]));
+                ra[1][i] = make_uint4(__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
+                                      __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7]));
+                continue;
+            }
             if (gm < g.M) {
                 ra[0][i] = load_row8<AL_A>(g.a_hi + gm * g.lda, gk, klim);
                 ra[1][i] = load_row8<AL_A>(g.a_lo + gm * g.lda, gk, klim);
@@ -313,6 +341,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
         for (int i = 0; i < T::A_CHUNKS; ++i) {
             const int c = tid + kThreads * i;
             const int kg = c & 7, row = c >> 3;
+            if constexpr (XF) {  // eight FP32 values -> the hi and lo granules
+                const floatx4_t x0 = __builtin_bit_cast(floatx4_t, ra[0][i]);
+                const floatx4_t x1 = __builtin_bit_cast(floatx4_t, ra[1][i]);
+                half8_t h, l;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    _Float16 hh, ll;
+                    split_value(e < 4 ? x0[e] : x1[e - 4], hh, ll);
+                    h[e] = hh;
+                    l[e] = ll;
+                }
+                s[a_slot<T>(0, kg, row)] = __builtin_bit_cast(uint4, h);
+                s[a_slot<T>(1, kg, row)] = __builtin_bit_cast(uint4, l);
+                continue;
+            }
             s[a_slot<T>(0, kg, row)] = ra[0][i];
             s[a_slot<T>(1, kg, row)] = ra[1][i];
         }
@@ -539,6 +582,16 @@ int64_t tiles_of(int64_t M, int64_t N)
     return ((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
 }
 
+constexpr int64_t kCus = 256;
+
+// The generic kernel's tile for an M x N output when the LDS-DMA kernel does
+// not run: 0 = 128 x 256, 1 = 64 x 128, 2 = 32 x 128 (see launch_gemm).
+int generic_tile(int64_t M, int64_t N)
+{
+    if (tiles_of<TileLarge>(M, N) >= kCus * 3 / 4) return 0;
+    return tiles_of<TileMedium>(M, N) >= kCus ? 1 : 2;
+}
+
 }  // namespace
 
 // Tile choice: the LDS-DMA kernel (128 x 256 tiles) from three quarters of
@@ -552,7 +605,6 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
                        const float *bias, bool w_nk, bool geglu_rmw)
 {
     GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias, geglu_rmw ? 1 : 0, 1, nullptr, 0};
-    constexpr int64_t kCus = 256;
     if (tiles_of<TileLarge>(M, N) >= kCus * 3 / 4 && !geglu_rmw) {
         const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
                                              a_zero_padded, stream, bias, w_nk);
@@ -562,6 +614,29 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
     if (tiles_of<TileMedium>(M, N) >= kCus)
         return w_nk ? launch_tile<TileMedium, 0, true>(g, stream) : launch_tile<TileMedium>(g, stream);
     return w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
+}
+
+// The projection in one launch on the grids that take the 32 x 128 tile:
+// x split in registers as its stages are loaded (the split dispatch and the
+// planes drop out; the bits are those of split + launch_gemm).
+hipError_t launch_gemm_xsplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias, bool w_nk)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || generic_tile(M, N) != 2) return hipErrorNotSupported;
+    if (ldx % 4 || !aligned16(x) || ldw % 8 || !aligned16(w)) return hipErrorNotSupported;
+    constexpr int64_t kLim = kNoOffset - (1 << 20);
+    const bool fits = (M + TileSmall::BM) * ldx * 4 < kLim &&
+                      (w_nk ? (N + TileSmall::BN) * ldw * 2 + (int64_t)kBK * 2 < kLim
+                            : (K + kBK) * ldw * 2 + (int64_t)TileSmall::BN * 2 < kLim);
+    if (!fits) return hipErrorNotSupported;
+    GemmArgs g{reinterpret_cast<const uint16_t *>(x), nullptr, ldx, w, ldw, y, ldy, nullptr, nullptr, 0, M, N, K,
+               bias, 0, 1, nullptr, 0};
+    const dim3 grid((unsigned)tiles_of<TileSmall>(M, N));
+    if (w_nk)
+        gemm_kernel<TileSmall, true, true, true, 0, true, true><<<grid, kThreads, 0, stream>>>(g);
+    else
+        gemm_kernel<TileSmall, true, true, true, 0, false, true><<<grid, kThreads, 0, stream>>>(g);
+    return hipGetLastError();
 }
 
 

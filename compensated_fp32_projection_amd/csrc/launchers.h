@@ -119,6 +119,16 @@ hipError_t launch_gemm_dma_split(const float *a, int64_t lda, const uint16_t *w,
                                  int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
                                  const float *bias = nullptr, bool w_nk = false);
 
+// The projection from FP32 x in one launch with the split in registers, for
+// the grids the generic kernel runs in its 32 x 128 tile (see gemm.hip);
+// the bits of launch_split + launch_gemm.  hipErrorNotSupported, with
+// nothing enqueued, for other grids, K == 0, or unless ldx % 4 == 0,
+// ldw % 8 == 0, x and W are 16-byte aligned and their byte offsets stay
+// below 2^31.
+hipError_t launch_gemm_xsplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias = nullptr,
+                              bool w_nk = false);
+
 // GEGLU-fused GEMM on split planes (see gemm_dma.hip); hipErrorNotSupported,
 // with nothing enqueued, when the LDS-DMA conditions do not hold.
 hipError_t launch_gemm_dma_geglu(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,

@@ -103,6 +103,11 @@ hipError_t launch_gemm_ksplit(const float *x, int64_t ldx, const uint16_t *w, in
     reached("launch_gemm_ksplit");
 }
 
+hipError_t launch_gemm_xsplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias, bool w_nk)
+{
+    reached("launch_gemm_xsplit");
+}
+
 hipError_t launch_gemm_ksplit_geglu(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int64_t up_off, float *out, int64_t ldo, int64_t M, int64_t F, int64_t K, hipStream_t stream, const float *bias)
 {
     reached("launch_gemm_ksplit_geglu");

@@ -373,18 +373,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             if (b < T::W_BLOCKS) {
                 const int kgw = b / (T::BN / 8), nc = b % (T::BN / 8);
                 // rw[j][r] holds W[k = 8*kgw + r][n = 8*nc .. 8*nc + 7]; gather
-                // column e into one granule of eight k values.
+                // column e into one granule of eight k values.  Each dword of
+                // the granule is one byte permute: the e-th halves of rows 2p
+                // (low half) and 2p + 1 (high half).
                 const uint32_t *v = reinterpret_cast<const uint32_t *>(rw[j]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int q = e >> 1, sh = 16 * (e & 1);
+                    const int q = e >> 1;
+                    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
                     uint32_t d[4];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t lo16 = (v[(2 * p) * 4 + q] >> sh) & 0xFFFFu;
-                        const uint32_t hi16 = (v[(2 * p + 1) * 4 + q] >> sh) & 0xFFFFu;
-                        d[p] = lo16 | (hi16 << 16);
-                    }
+                    for (int p = 0; p < 4; ++p)
+                        d[p] = __builtin_amdgcn_perm(v[(2 * p + 1) * 4 + q], v[(2 * p) * 4 + q], sel);
                     s[w_slot<T>(kgw, 8 * nc + e)] = make_uint4(d[0], d[1], d[2], d[3]);
                 }
             }

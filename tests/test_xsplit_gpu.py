@@ -115,6 +115,22 @@ def test_xsplit_qkv_workload_and_layouts():
     assert_within_tolerance(y, y64, abs64, "qkv")
 
 
+@pytest.mark.parametrize("M,K,N,ldx", [(512, 100, 2304, 100), (520, 1003, 2304, 1004), (600, 7, 2000, 8)])
+def test_xsplit_k_not_multiple_of_8(M, K, N, ldx):
+    """K % 8 != 0 (or K < 64: only a ragged stage), rows padded to a multiple
+    of 4 floats so that they stay 16-byte aligned: one launch, the bits of
+    split + GEMM."""
+    assert small_tile_grid(M, N)
+    A, W = workloads.random_case(M * 3 + K + N, M, K, N, a_scale=20.0)
+    note(f"xsplit ragged K {M}x{K}x{N} ldx={ldx}")
+    y, launches = linear(A, W, ldx=ldx)
+    assert launches in (None, 1), f"{launches} launches"
+    y2 = two_launch(A, W)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32)), "not the bits of split + GEMM"
+    y64, abs64 = oracle.y64(A, W)
+    assert_within_tolerance(y, y64, abs64, f"xsplit {M}x{K}x{N}")
+
+
 def test_xsplit_unaligned_rows_fall_back():
     """Rows of x 4-byte but not 16-byte aligned (ldx % 4 != 0): split +
     GEMM (two launches), the same bits."""

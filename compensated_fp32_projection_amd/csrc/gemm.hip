@@ -16,7 +16,9 @@
 //   * K advances in stages of 64.  A stage of A_hi, A_lo and W is loaded from
 //     global memory into registers while the previous stage is multiplied out
 //     of LDS, then written to the other half of a double-buffered LDS area:
-//     one barrier per stage.
+//     one barrier per stage.  The 32 x 128 tile, which runs the smallest
+//     grids, keeps two register sets and so loads two stages ahead, and can
+//     take FP32 x and split it in registers (one launch for the projection).
 //   * LDS holds 16-byte "k-granules" (8 consecutive k of one row or one
 //     column), which is the per-lane operand shape of the MFMA, so every
 //     fragment read is one 16-byte LDS read.  W arrives N-contiguous from

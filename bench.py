@@ -221,7 +221,7 @@ def _rel_err(y, y64, abs64):
     return float(e.max()), float(np.sqrt(np.mean(e * e)))
 
 
-def measure_configs(stream, with_cpu: bool):
+def measure_configs(stream, with_cpu: bool, only=None):
     """Each workload through cfp32_linear on its own: microseconds per call
     (median of timed loops of at least 1 ms), kernel launches per call,
     FP32-equivalent TFLOP/s with the FP16-MFMA fraction (both products) or
@@ -232,7 +232,8 @@ def measure_configs(stream, with_cpu: bool):
     oracle's median of 3 runs (configs 1-3 and 5a; one run for config 4),
     the FP64 reference's time (for information), the SHA-256 of the input
     arrays (the same bytes the oracle and the GPU receive) and the FP16
-    library GEMM (torch.matmul on FP16 x, one product, context only)."""
+    library GEMM (torch.matmul on FP16 x, one product, context only).
+    `only`: the workload ids to measure (e.g. {"2", "5a"}), or None for all."""
     import numpy as np
     import torch
 
@@ -249,6 +250,8 @@ def measure_configs(stream, with_cpu: bool):
              ("5a_decode", pair.A[0], pair.W),
              ("5b_ffn_prefill", pair.A[1], pair.W)]
     del pair
+    if only is not None:
+        cases = [c for c in cases if c[0].split("_")[0] in only]
     out = {}
     threads = oracle.num_threads()
     for name, A, W in cases:
@@ -557,6 +560,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-per-thread", type=int, default=40)
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--configs", default="all",
+                    help="workloads of the per-workload table: comma-separated ids out of 1,2,3,4,5a,5b, or all")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"also run one plain device copy of {CALIB_BYTES} bytes (counter scaling reference)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT"),
@@ -582,6 +587,10 @@ def main():
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.profile_command)
         return
+    if args.configs != "all":
+        unknown = set(args.configs.split(",")) - {"1", "2", "3", "4", "5a", "5b"}
+        if unknown:
+            ap.error(f"--configs: unknown workload ids {sorted(unknown)} (known: 1,2,3,4,5a,5b)")
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -759,7 +768,8 @@ def main():
             4096, 4096, 4096, kpa, sh), "separate add"), 10)
     torch.cuda.synchronize()
 
-    configs = None if args.no_configs else measure_configs(stream, with_cpu=not args.no_cpu_baseline)
+    only = None if args.configs == "all" else set(args.configs.split(","))
+    configs = None if args.no_configs else measure_configs(stream, with_cpu=not args.no_cpu_baseline, only=only)
 
     if args.calibration_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)

@@ -191,7 +191,12 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         x on the way into LDS (the workspace is then not touched; both give
  *         identical bits); or, for M <= 64 with fewer than 128 tiles and
  *         K % 8 == 0, the split, a GEMM over chunks of K writing FP32 partial
- *         sums into the workspace, and a merge dispatch (three launches).
+ *         sums into the workspace, and a merge dispatch (three launches); or,
+ *         on grids the GEMM runs in 32 x 128 tiles (fewer than 192 tiles of
+ *         128 x 256 and fewer than 256 of 64 x 128) with ldx % 4 == 0,
+ *         ldw % 8 == 0 and x, w 16-byte aligned, one GEMM launch that splits
+ *         x in registers as it loads it (the workspace is then not touched;
+ *         the bits of the two launches).
  * Every path sums in a fixed order: results repeat bit for bit.
  * Results satisfy |y - y_exact| <= 1e-5 * sum_k |x_k w_k| for inputs within
  * the split's domain (|x| < 65520). */

@@ -319,15 +319,18 @@ __global__ __launch_bounds__(kT) void gemv_mfma_kernel(GemvArgs g)
 // kernel (its 16 waves per block keep more loads in flight; at M <= 2 the
 // FP32 FMAs cost little).  A block of 1024 threads owns one 512-column tile
 // of one chunk; wave v takes rows r0 + v, r0 + v + 16, ... and lane l columns
-// 8l .. 8l + 7, with 8 rows of loads (1 KiB each, streaming policy) in
-// flight; x is read with scalar loads (every lane needs the same value).
+// 8l .. 8l + 7, with 16 rows of loads (1 KiB each, streaming policy) in
+// flight (8 measured the same at 1 x 4096 x 14336 and 2.9 us slower at
+// 1 x 8192 x 4096, whose 256-row chunks then took two rounds per wave; 92 /
+// 126 registers for one / two rows keep four waves per SIMD); x is read
+// with scalar loads (every lane needs the same value).
 // Products hi * w and lo * w accumulate with FP32 fused multiply-adds (the
 // FP16 x FP16 product is exact, so each step rounds once, as in the matrix
 // unit).  The 16 waves are summed in index order through LDS; the block then
 // writes its chunk's partial sums, or merges and writes y when K is one
 // chunk.
 constexpr int kValuThreads = 1024;
-constexpr int kValuU = 8;
+constexpr int kValuU = 16;
 
 template <int MR>
 __global__ __launch_bounds__(kValuThreads) void gemv_valu_kernel(GemvArgs g)

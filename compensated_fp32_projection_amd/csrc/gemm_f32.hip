@@ -12,18 +12,24 @@
 //     eighth of the FP16 rate the compensated path's two products share.
 //   * 256 threads (4 waves), a 128 x 128 output tile, each wave 64 x 64:
 //     4 x 4 blocks of 16 x 16, 64 accumulators per lane.  K advances in
-//     stages of 16 through two LDS buffers, loaded through registers (A as
-//     FP32, W as FP16 widened to FP32 on the way into LDS).
-//   * K order inside a stage: MFMA step j (0..3) of lane group q = lane / 16
-//     multiplies physical k = 4 q + j.  A and B use the same mapping, so every
-//     output still sums each product exactly once; in exchange a lane's four
-//     A values of a stage (row r, k = 4q .. 4q + 3) and its four B values
-//     (column c, the same k) are each one ds_read_b128: A sits in LDS row-major
-//     and W column-major ([n][k]), rows padded to 20 floats so that the eight
-//     lanes of one 128-byte read touch eight different bank groups.
-//   * Out-of-range rows, columns and k read as zero and are not stored: any
-//     M, N, K >= 0 works; 16-byte global loads where the pointers and leading
-//     dimensions allow them, element loads otherwise.
+//     stages of 32 through two LDS buffers, loaded through registers (A as
+//     FP32, W as FP16 widened to FP32 on the way into LDS); 72 KiB of LDS
+//     and at most 256 registers give two blocks (two waves per SIMD) per CU.
+//   * K order inside each 16-deep half of a stage: MFMA step j (0..3) of
+//     lane group q = lane / 16 multiplies physical k = 4 q + j.  A and B use
+//     the same mapping, so every output still sums each product exactly
+//     once; in exchange a lane's four A values (row r, k = 4q .. 4q + 3) and
+//     its four B values (column c, the same k) are each one ds_read_b128: A
+//     sits in LDS row-major and W column-major ([n][k]), rows padded to 36
+//     floats so that the eight lanes of one 128-byte read touch eight
+//     different bank groups.  The order does not depend on the stage depth.
+//   * Full stages of 16-byte-loadable operands are fetched with raw buffer
+//     loads at per-lane offsets (rows past M and columns past N at an offset
+//     no buffer reaches, which reads zero): no branch in the main loop, so
+//     the compiler's wait for a stage's registers does not also wait for the
+//     next stage's loads.  The ragged last stage, and operands that do not
+//     allow 16-byte loads, take guarded element loads.  Any M, N, K >= 0
+//     works.
 #include "device_common.h"
 #include "launchers.h"
 #include "tile_order.h"
@@ -33,15 +39,21 @@ namespace cfp32 {
 namespace {
 
 constexpr int kF32Threads = 256;
-constexpr int kF32BM = 128, kF32BN = 128, kF32BK = 16;
-constexpr int kF32Ld = 20;  // LDS floats per row of 16 k (16 + 4 pad)
+constexpr int kF32BM = 128, kF32BN = 128, kF32BK = 32;
+constexpr int kF32Ld = kF32BK + 4;            // LDS floats per row of a stage (+ 4 pad)
+constexpr int kF32Chunks = kF32BK / 16;       // 8-element loads per thread per stage, for A and for W
+constexpr int kF32NoOffset = 0x7FFFFFF0;      // a raw buffer load here reads zero
+constexpr int kF32Word3 = 0x00020000;         // raw 32-bit buffer, gfx9 family
 
-template <bool AV, bool WV>
+// BUF: x and W allow 16-byte loads and every byte offset the kernel forms
+// stays below 2^31 (checked by the launcher).
+template <bool AV, bool WV, bool BUF>
 __global__ __launch_bounds__(kF32Threads) void gemm_f32_kernel(const float *__restrict__ A, int64_t lda,
                                                                const uint16_t *__restrict__ W, int64_t ldw,
                                                                float *__restrict__ Y, int64_t ldy, int64_t M,
                                                                int64_t N, int64_t K)
 {
+    static_assert(!BUF || (AV && WV), "buffer loads need 16-byte-loadable operands");
     __shared__ float sA[2][kF32BM * kF32Ld];
     __shared__ float sW[2][kF32BN * kF32Ld];
 
@@ -57,43 +69,77 @@ __global__ __launch_bounds__(kF32Threads) void gemm_f32_kernel(const float *__re
     tile_of_block(blockIdx.x, nbm, nbn, tile_m, tile_n);
     const int64_t m0 = tile_m * kF32BM, n0 = tile_n * kF32BN;
 
-    // Loaders: A row t / 2, k 8 (t % 2) .. + 7; W k-row t / 16, columns
-    // 8 (t % 16) .. + 7.
-    const int a_row = tid >> 1, a_k = 8 * (tid & 1);
-    const int w_k = tid >> 4, w_n = 8 * (tid & 15);
-    float ra[8];
-    float rw[8];
+    // Loaders, chunk c = tid + 256 i: A row c / 4, k 8 (c % 4) .. + 7; W
+    // k-row c / 16, columns 8 (c % 16) .. + 7.
+    int a_row[kF32Chunks], a_k[kF32Chunks], w_k[kF32Chunks], w_n[kF32Chunks];
+#pragma unroll
+    for (int i = 0; i < kF32Chunks; ++i) {
+        const int c = tid + kF32Threads * i;
+        a_row[i] = c / (kF32BK / 8);
+        a_k[i] = 8 * (c % (kF32BK / 8));
+        w_k[i] = c / (kF32BN / 8);
+        w_n[i] = 8 * (c % (kF32BN / 8));
+    }
+    float ra[kF32Chunks][8];
+    uint4 rw[kF32Chunks];  // eight FP16 W values, widened when written to LDS
 
-    auto load_stage = [&](int64_t k0) {
-        const int64_t gm = m0 + a_row;
-        const int64_t gk = k0 + a_k;
-        if (AV && gm < M && gk + 8 <= K) {
-            const floatx4_t v0 = *reinterpret_cast<const floatx4_t *>(A + gm * lda + gk);
-            const floatx4_t v1 = *reinterpret_cast<const floatx4_t *>(A + gm * lda + gk + 4);
+    const __amdgpu_buffer_rsrc_t rs_a =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(A), 0, BUF ? (int)(M * lda * 4) : 0, kF32Word3);
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(W), 0, BUF ? (int)(K * ldw * 2) : 0, kF32Word3);
+    int voff_a[kF32Chunks], voff_w[kF32Chunks];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ra[e] = v0[e], ra[e + 4] = v1[e];
-        } else {
+    for (int i = 0; i < kF32Chunks; ++i) {
+        const int64_t gm = m0 + a_row[i], gn = n0 + w_n[i];
+        voff_a[i] = BUF && gm < M ? (int)((gm * lda + a_k[i]) * 4) : kF32NoOffset;
+        voff_w[i] = BUF && gn < N ? (int)((w_k[i] * ldw + gn) * 2) : kF32NoOffset;
+    }
+
+    // A full stage (k0 + 32 <= K), no branch; the stage's k offset travels
+    // in the scalar offset (wave-uniform).
+    auto load_stage_buf = [&](int64_t k0) __attribute__((always_inline)) {
+        const int so_a = __builtin_amdgcn_readfirstlane((int)(k0 * 4));
+        const int so_w = __builtin_amdgcn_readfirstlane((int)(k0 * ldw * 2));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ra[e] = (gm < M && gk + e < K) ? A[gm * lda + gk + e] : 0.0f;
-        }
-        const int64_t wk = k0 + w_k;
-        const int64_t wcol = n0 + w_n;
-        if (wk < K) {
-            const uint4 v = load_row8<WV>(W + wk * ldw, wcol, N);
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < kF32Chunks; ++i) {
+            const floatx4_t v0 = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[i], so_a, 0));
+            const floatx4_t v1 =
+                __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[i] + 16, so_a, 0));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) rw[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) rw[e] = 0.0f;
+            for (int e = 0; e < 4; ++e) ra[i][e] = v0[e], ra[i][e + 4] = v1[e];
+            rw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[i], so_w, 0));
         }
     };
-    auto store_stage = [&](int buf) {
-        float *pa = &sA[buf][a_row * kF32Ld + a_k];
-        *reinterpret_cast<floatx4_t *>(pa) = floatx4_t{ra[0], ra[1], ra[2], ra[3]};
-        *reinterpret_cast<floatx4_t *>(pa + 4) = floatx4_t{ra[4], ra[5], ra[6], ra[7]};
+    // Any stage: rows past M, k past K and columns past N read as zero.
+    auto load_stage = [&](int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sW[buf][(w_n + e) * kF32Ld + w_k] = rw[e];
+        for (int i = 0; i < kF32Chunks; ++i) {
+            const int64_t gm = m0 + a_row[i];
+            const int64_t gk = k0 + a_k[i];
+            if (AV && gm < M && gk + 8 <= K) {
+                const floatx4_t v0 = *reinterpret_cast<const floatx4_t *>(A + gm * lda + gk);
+                const floatx4_t v1 = *reinterpret_cast<const floatx4_t *>(A + gm * lda + gk + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ra[i][e] = v0[e], ra[i][e + 4] = v1[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ra[i][e] = (gm < M && gk + e < K) ? A[gm * lda + gk + e] : 0.0f;
+            }
+            const int64_t wk = k0 + w_k[i];
+            rw[i] = wk < K ? load_row8<WV>(W + wk * ldw, n0 + w_n[i], N) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kF32Chunks; ++i) {
+            float *pa = &sA[buf][a_row[i] * kF32Ld + a_k[i]];
+            *reinterpret_cast<floatx4_t *>(pa) = floatx4_t{ra[i][0], ra[i][1], ra[i][2], ra[i][3]};
+            *reinterpret_cast<floatx4_t *>(pa + 4) = floatx4_t{ra[i][4], ra[i][5], ra[i][6], ra[i][7]};
+            const uint32_t d[4] = {rw[i].x, rw[i].y, rw[i].z, rw[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sW[buf][(w_n[i] + e) * kF32Ld + w_k[i]] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
     };
 
     floatx4_t acc[4][4];
@@ -102,33 +148,54 @@ __global__ __launch_bounds__(kF32Threads) void gemm_f32_kernel(const float *__re
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{};
 
-    auto compute = [&](int buf) {
-        floatx4_t a[4], b[4];
+    auto compute = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a[i] = *reinterpret_cast<const floatx4_t *>(&sA[buf][(64 * wm + 16 * i + r) * kF32Ld + 4 * q]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *reinterpret_cast<const floatx4_t *>(&sW[buf][(64 * wn + 16 * j + r) * kF32Ld + 4 * q]);
-#pragma unroll
-        for (int step = 0; step < 4; ++step)
+        for (int h = 0; h < kF32BK / 16; ++h) {
+            floatx4_t a[4], b[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const floatx4_t *>(&sA[buf][(64 * wm + 16 * i + r) * kF32Ld + 16 * h + 4 * q]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][step], b[j][step], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+                b[j] = *reinterpret_cast<const floatx4_t *>(&sW[buf][(64 * wn + 16 * j + r) * kF32Ld + 16 * h + 4 * q]);
+#pragma unroll
+            for (int step = 0; step < 4; ++step)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][step], b[j][step], acc[i][j], 0, 0, 0);
+        }
     };
 
+    // Stage s is multiplied out of LDS buffer s & 1 while stage s + 1 is
+    // fetched into registers; one barrier per stage.
     const int64_t nk = (K + kF32BK - 1) / kF32BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int64_t s = 0; s < nk; ++s) {
-        const bool more = s + 1 < nk;
-        if (more) load_stage((s + 1) * kF32BK);
-        compute((int)(s & 1));
-        if (more) store_stage((int)((s + 1) & 1));
+    const int64_t nk_full = BUF ? K / kF32BK : 0;
+    if (nk > 0) {
+        if (nk_full > 0)
+            load_stage_buf(0);
+        else
+            load_stage(0);
+        store_stage(0);
         __syncthreads();
+        int64_t s = 0;
+        for (; s + 1 < nk_full; ++s) {
+            load_stage_buf((s + 1) * kF32BK);
+            // Keep the loads ahead of the MFMAs: scheduled after them (to
+            // reuse the fragment registers) they would not overlap compute.
+            __builtin_amdgcn_sched_barrier(0);
+            compute((int)(s & 1));
+            store_stage((int)((s + 1) & 1));
+            __syncthreads();
+        }
+        for (; s + 1 < nk; ++s) {
+            load_stage((s + 1) * kF32BK);
+            compute((int)(s & 1));
+            store_stage((int)((s + 1) & 1));
+            __syncthreads();
+        }
+        compute((int)(s & 1));
     }
 
     // 16 x 16 accumulator: lane holds column r, rows 4 q + e of its block.
@@ -155,15 +222,21 @@ hipError_t launch_gemm_f32(const float *x, int64_t ldx, const uint16_t *w, int64
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const bool av = (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
     const bool wv = (ldw % 8 == 0) && ((reinterpret_cast<uintptr_t>(w) & 15) == 0);
+    // Buffer offsets are 32-bit: every byte offset a thread forms, including
+    // a tile's overhang past M and N and a stage's past K, stays below this.
+    constexpr int64_t kLim = kF32NoOffset - (1 << 20);
+    const bool fits = (M + kF32BM) * ldx * 4 < kLim && (K + kF32BK) * ldw * 2 + (int64_t)kF32BN * 2 < kLim;
     const dim3 grid((unsigned)blocks);
-    if (av && wv)
-        gemm_f32_kernel<true, true><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
+    if (av && wv && fits)
+        gemm_f32_kernel<true, true, true><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
+    else if (av && wv)
+        gemm_f32_kernel<true, true, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
     else if (av)
-        gemm_f32_kernel<true, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
+        gemm_f32_kernel<true, false, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
     else if (wv)
-        gemm_f32_kernel<false, true><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
+        gemm_f32_kernel<false, true, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
     else
-        gemm_f32_kernel<false, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
+        gemm_f32_kernel<false, false, false><<<grid, kF32Threads, 0, stream>>>(x, ldx, w, ldw, y, ldy, M, N, K);
     return hipGetLastError();
 }
 

@@ -23,12 +23,14 @@ pytestmark = pytest.mark.gpu
 
 
 # [K, N] weights: the small-M product + merge dispatches, the generic small-M
-# kernel, split + GEMM.  [N, K] weights: the one-dispatch small-M kernel (one
-# and three groups of 8 rows) and the GEMM with 64-deep W stages.
+# kernel, the small-grid kernel, the generic GEMM's 32 x 128 tile with the
+# split in registers.  [N, K] weights: the one-dispatch small-M kernel (one
+# and three groups of 8 rows), the small-grid kernel and the 32 x 128 tile.
 @pytest.mark.parametrize("shared_ws", [False, True])
 @pytest.mark.parametrize("M,K,N,layout", [(1, 4096, 14336, "kn"), (4, 1000, 520, "kn"), (2, 24, 40, "kn"),
-                                          (12, 2048, 3000, "kn"), (300, 512, 768, "kn"), (1, 4096, 14336, "nk"),
-                                          (20, 1024, 3000, "nk"), (300, 512, 768, "nk")])
+                                          (12, 2048, 3000, "kn"), (300, 512, 768, "kn"), (512, 776, 2304, "kn"),
+                                          (1, 4096, 14336, "nk"), (20, 1024, 3000, "nk"), (300, 512, 768, "nk"),
+                                          (600, 200, 2000, "nk")])
 def test_linear_replays_match_eager(M, K, N, layout, shared_ws):
     A, W = workloads.random_case(M + K + N, M, K, N, a_scale=4.0)
     dw = to_dev(W if layout == "kn" else np.ascontiguousarray(W.T)).view(torch.float16)

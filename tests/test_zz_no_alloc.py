@@ -49,7 +49,7 @@ def without(A, W):
 
 # (first, second) shapes M, K, N; the second call is smaller.
 PAIRS = [
-    ((4096, 4096, 8192), (512, 768, 2304)),    # split + GEMM, planes of exactly 64 MiB; then smaller planes
+    ((4096, 4096, 8192), (512, 768, 2304)),    # split + GEMM, planes of exactly 64 MiB; then no planes (split in registers)
     ((1, 4096, 14336), (3, 1000, 520)),        # small-M partial sums, twice
     ((64, 4096, 14336), (16, 2048, 3000)),     # split K (planes + partial sums); two groups of 8 rows
     ((8192, 4096, 14336), (333, 1000, 777)),   # planes of 128 MiB: split inside; then the generic GEMM

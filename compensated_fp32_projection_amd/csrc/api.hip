@@ -427,11 +427,13 @@ cfp32_status cfp32_linear_noalloc(const float *x, int64_t ldx, const uint16_t *w
     }
     const size_t need = cfp32_linear_ex_workspace_bytes(M, N, K, CFP32_W_KN);
     if (need == 0 && M > cfp32::kGemvMaxRows && K > 0) return CFP32_ERR_INVALID_VALUE;  // as in cfp32_linear_ex
-    // Above 64 rows cfp32_linear splits x into planes and runs one GEMM, or
-    // splits inside the GEMM; both give the same bits.  When the planes do
-    // not fit the scratch, only the second is possible.
+    // Where cfp32_linear does not split K it splits x into planes and runs
+    // one GEMM, or splits inside the GEMM; both give the same bits.  When the
+    // planes do not fit the scratch, only the second is possible; a split of
+    // K needs its partial sums, so without room for them there is no path
+    // with cfp32_linear's bits.
     const bool fits = need == 0 || need - kAlign <= kScratchBytes;
-    if (!fits && M <= 64) return CFP32_ERR_TOO_LARGE;
+    if (!fits && (M <= 64 || cfp32::gemm_split_plan(M, N, K).chunks > 1)) return CFP32_ERR_TOO_LARGE;
     cfp32_status st = check_device();
     if (st != CFP32_OK) return st;
     hipStream_t s = (hipStream_t)stream;

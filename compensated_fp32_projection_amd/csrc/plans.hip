@@ -53,14 +53,22 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
 {
     GemmSplitPlan p{1, 0, 0};
     // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
-    // 35-52 us; at M = 128 and 256 it measured no better than the generic
-    // kernel (75 vs 78 us, 122 vs 98 us), the partial sums costing what the
-    // wider grid gains.
-    constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kMaxRows = 64;
-    if (M <= kGemvMaxRows || M > kMaxRows || N <= 0 || K <= 0 || K % 8) return p;
+    // 35-52 us.  Above 64 rows the grid of 128 x 256 tiles must stay below
+    // the LDS-DMA kernel's own threshold (192 tiles), the chunks must bring
+    // it to at least 192 blocks, and the partial sums may take up to W's
+    // bytes and 56 MiB: x W at 96 / 128 / 192 / 256 x 4096 x 14336 went from
+    // 76.6 / 82.2 / 92.1 / 102.6 us (generic 32 x 128 tile) to 56.1 / 64.6 /
+    // 75.2 / 89.2 us, 128 x 8192 x 14336 from 159 to 97 us; where K per
+    // chunk is short (2048 x 1024 x 2048: 39 -> 55 us; 1024^3: 20 -> 33 us)
+    // or the blocks stay few (96 x 4096 x 4096: 28 -> 39 us against the
+    // small-grid kernel) it lost, which the conditions keep out.
+    constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kSmallRows = 64;
+    constexpr int64_t kMinBlocksWide = 192;
+    constexpr int64_t kMaxPartBytesWide = (int64_t)56 << 20;
+    if (M <= kGemvMaxRows || N <= 0 || K <= 0 || K % 8) return p;
     if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
     const int64_t tiles = ((M + kTileRows - 1) / kTileRows) * ((N + kTileCols - 1) / kTileCols);
-    if (tiles >= 128) return p;
+    if (tiles >= (M <= kSmallRows ? 128 : 192)) return p;
     int64_t c = 256 / tiles;
     for (int64_t cc = c; cc >= 1 && cc > c - 8; --cc)
         if ((cc * tiles) % 8 == 0) {
@@ -69,12 +77,21 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
         }
     const int64_t units = (K + kUnit - 1) / kUnit;
     if (c > units / kMinUnits) c = units / kMinUnits;
-    // The partial sums (8 M N bytes per chunk, written and read back) stay
-    // within a quarter of W's 2 K N bytes.
-    if (c > K / (16 * M)) c = K / (16 * M);
+    const int64_t n_pad = (N + 63) / 64 * 64;
+    if (M <= kSmallRows) {
+        // The partial sums (8 M N bytes per chunk, written and read back)
+        // stay within a quarter of W's 2 K N bytes.
+        if (c > K / (16 * M)) c = K / (16 * M);
+    } else {
+        // Within W's bytes and 56 MiB, and enough blocks to fill the GPU.
+        if (c > K / (4 * M)) c = K / (4 * M);
+        const int64_t cap = kMaxPartBytesWide / (M * 2 * n_pad * (int64_t)sizeof(float));
+        if (c > cap) c = cap;
+        if (c * tiles < kMinBlocksWide) return p;
+    }
     if (c < 2) return p;
     p.chunks = c;
-    p.n_pad = (N + 63) / 64 * 64;
+    p.n_pad = n_pad;
     p.workspace_bytes = (size_t)c * (size_t)M * 2u * (size_t)p.n_pad * sizeof(float);
     return p;
 }

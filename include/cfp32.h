@@ -148,9 +148,10 @@ CFP32_API cfp32_status cfp32_merge(const float *c_hi, const float *c_lo, int64_t
  * is needed: an empty problem, M, N or K == 0).  Returns 0 for negative
  * sizes.  M <= 8: about chunks * M * N * 8 bytes of FP32 partial sums, with
  * at most 256 chunks (1 MiB for M = 1, N = 14336, K = 4096).
- * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes, plus, for
- * M <= 64 on small grids, FP32 partial sums of split K (at most a quarter
- * of W's bytes); for M <= 16 at least the small-M partial sums.  M > 8
+ * M > 8: the FP16 hi and lo planes of x, about 4 * M * K bytes, plus, on
+ * small grids, FP32 partial sums of split K (at most a quarter of W's bytes
+ * for M <= 64; above, at most W's bytes and 56 MiB); for M <= 16 at least
+ * the small-M partial sums.  M > 8
  * with N not a multiple of 8: also a padded copy of W, 2 * K * N8 bytes
  * (N8 = N rounded up to 8).  Returns 0 too when these sizes would pass
  * 2^48 elements; cfp32_linear then refuses the shape. */
@@ -189,9 +190,12 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
  *         ldw % 8 == 0, x and w 16-byte aligned, one GEMM launch that splits
  *         x on the way into LDS (the workspace is then not touched; both give
- *         identical bits); or, for M <= 64 with fewer than 128 tiles and
- *         K % 8 == 0, the split, a GEMM over chunks of K writing FP32 partial
- *         sums into the workspace, and a merge dispatch (three launches); or,
+ *         identical bits); or, on small grids with K % 8 == 0 (M <= 64
+ *         with fewer than 128 tiles; above, fewer than 192 tiles where K is
+ *         long enough to give each of at least 192 blocks four 64-deep
+ *         units, with the partial sums within W's bytes and 56 MiB), the
+ *         split, a GEMM over chunks of K writing FP32 partial sums into the
+ *         workspace, and a merge dispatch (three launches); or,
  *         on grids the GEMM runs in 32 x 128 tiles (fewer than 192 tiles of
  *         128 x 256 and fewer than 256 of 64 x 128) with ldx % 4 == 0,
  *         ldw % 8 == 0 and x, w 16-byte aligned, one GEMM launch that splits
@@ -213,10 +217,11 @@ CFP32_API cfp32_status cfp32_linear(const float *x, int64_t ldx, const uint16_t 
  * when the library's code is loaded on a device and held until the process
  * ends.  This call allocates and frees nothing.
  *   - Problems whose scratch exceeds 64 MiB return CFP32_ERR_TOO_LARGE with
- *     nothing enqueued; above 64 rows, such problems instead run the GEMM
- *     that splits x on the way into LDS and needs no scratch (same bits as
- *     cfp32_linear), when x and W allow it (K % 4 == 0, ldx % 4 == 0,
- *     ldw % 8 == 0, 16-byte aligned), else CFP32_ERR_TOO_LARGE.  cfp32_linear_
+ *     nothing enqueued; above 64 rows, where cfp32_linear does not split K
+ *     across blocks, such problems instead run the GEMM that splits x on the
+ *     way into LDS and needs no scratch (same bits as cfp32_linear), when x
+ *     and W allow it (K % 4 == 0, ldx % 4 == 0, ldw % 8 == 0, 16-byte
+ *     aligned), else CFP32_ERR_TOO_LARGE.  cfp32_linear_
  *     workspace_bytes(M, N, K) - 256 is the scratch a shape needs.
  *   - Every call on one device shares that device's array, which keeps the
  *     last call's contents; nothing in it needs to start at zero (each

@@ -1,5 +1,7 @@
 """GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
-(8 < M <= 64, fewer than 128 output tiles of 128 x 256):
+(8 < M <= 64, fewer than 128 output tiles of 128 x 256; above 64 rows,
+fewer than 192 tiles where K gives at least 192 blocks of four 64-deep
+units):
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
     units, each chunk's C_hi, C_lo go to FP32 partial sums, and a merge
     dispatch adds them in chunk order and merges once.  The plan depends on
@@ -125,3 +127,28 @@ def test_bias_is_one_addition(M, K, N, layout):
     y0 = run(A, W, layout=layout)
     y1 = run(A, W, layout=layout, bias=bias)
     assert np.array_equal(y1.view(np.uint32), (y0 + bias[None, :]).astype(np.float32).view(np.uint32))
+
+
+# (M, K, N) above 64 rows: the batched FFN shape (four chunks), ragged M, N
+# and a ragged last unit of K, three chunks with 192 blocks, ragged M with
+# many chunks.
+WIDE_SPLIT = [(96, 4096, 14336), (200, 4000, 10000), (256, 4096, 8192), (130, 8192, 2056)]
+
+
+@pytest.mark.parametrize("M,K,N", WIDE_SPLIT)
+def test_split_k_above_64_rows(M, K, N):
+    """The same cut of K from every kernel (LDS-DMA with aligned weights in
+    both layouts, the generic kernel with unaligned ones): identical bits,
+    within tolerance of FP64, below the single-FP16 error, repeatable."""
+    need = cf.cfp32_linear_ex_workspace_bytes(M, N, K, cf.W_NK)
+    assert need > planes_bytes(M, K) + 256, "shape does not take the split-K path"
+    A, W = workloads.random_case(M * 5 + K + 3 * N, M, K, N, a_scale=20.0)
+    note(f"split-K above 64 rows {M}x{K}x{N}")
+    y = run(A, W)
+    check(y, A, W, f"split-K {M}x{K}x{N}")
+    for other in (run(A, W, layout=cf.W_NK), run(A, W, w_offset=1), run(A, W, layout=cf.W_NK, w_offset=1)):
+        assert np.array_equal(y.view(np.uint32), other.view(np.uint32)), "kernels cut K differently"
+    assert np.array_equal(y.view(np.uint32), run(A, W).view(np.uint32)), "not deterministic"
+    bias = (np.random.default_rng(M).standard_normal(N) * 3).astype(np.float32)
+    yb = run(A, W, bias=bias)
+    assert np.array_equal(yb.view(np.uint32), (y + bias[None, :]).astype(np.float32).view(np.uint32))

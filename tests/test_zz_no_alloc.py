@@ -6,10 +6,11 @@ first (the array keeps the first call's contents, which must not matter),
 its output equals cfp32_linear's with a workspace bit for bit, on each path:
 the small-M dispatches (partial sums in the array), split K over a small grid
 (planes and partial sums), split + GEMM (planes exactly filling the 64 MiB),
-the generic GEMM for unaligned shapes, and, above 64 rows, a problem whose
-planes would not fit, which runs the GEMM that splits inside (no scratch).
-A problem that cannot run within the array is refused with
-CFP32_ERR_TOO_LARGE and writes nothing.
+the generic GEMM for unaligned shapes, split K above 64 rows, and, above 64
+rows, a problem whose planes would not fit, which runs the GEMM that splits
+inside (no scratch).  A problem that cannot run within the array (or whose
+split of K needs more than it holds) is refused with CFP32_ERR_TOO_LARGE and
+writes nothing.
 """
 import numpy as np
 import pytest
@@ -53,6 +54,7 @@ PAIRS = [
     ((1, 4096, 14336), (3, 1000, 520)),        # small-M partial sums, twice
     ((64, 4096, 14336), (16, 2048, 3000)),     # split K (planes + partial sums); two groups of 8 rows
     ((8192, 4096, 14336), (333, 1000, 777)),   # planes of 128 MiB: split inside; then the generic GEMM
+    ((256, 4096, 14336), (96, 4096, 14336)),   # split K above 64 rows (63 MB of planes and partial sums), twice
 ]
 
 
@@ -77,6 +79,22 @@ def test_noalloc_refuses_what_does_not_fit():
     dx, dw = to_dev(A), to_dev(W)
     y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
     note("noalloc refusal 5000x4001x300")
+    st = cf.cfp32_linear_noalloc(dx.data_ptr(), K, dw.data_ptr(), N, y.data_ptr(), N, M, N, K, stream_handle())
+    assert st == cf.ERR_TOO_LARGE
+    assert (to_host(y) == 7.0).all()
+
+
+def test_noalloc_refuses_a_split_of_k_that_does_not_fit():
+    """Above 64 rows on a small grid cfp32_linear splits K across blocks;
+    when its planes and partial sums (here 21 MB and 50 MB) exceed the
+    array, no path with its bits is left: refused, y untouched."""
+    M, K, N = 256, 20480, 8192
+    need = cf.cfp32_linear_workspace_bytes(M, N, K)
+    assert need - 256 > SCRATCH
+    dx = torch.zeros((M, K), dtype=torch.float32, device="cuda")
+    dw = torch.zeros((K, N), dtype=torch.int16, device="cuda")
+    y = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    note("noalloc refusal 256x20480x8192")
     st = cf.cfp32_linear_noalloc(dx.data_ptr(), K, dw.data_ptr(), N, y.data_ptr(), N, M, N, K, stream_handle())
     assert st == cf.ERR_TOO_LARGE
     assert (to_host(y) == 7.0).all()

@@ -590,24 +590,27 @@ constexpr int64_t kCus = 256;
 // not run: 0 = 128 x 256, 1 = 64 x 128, 2 = 32 x 128 (see launch_gemm).
 int generic_tile(int64_t M, int64_t N)
 {
-    if (tiles_of<TileLarge>(M, N) >= kCus * 3 / 4) return 0;
+    if (tiles_of<TileLarge>(M, N) >= kCus / 2) return 0;
     return tiles_of<TileMedium>(M, N) >= kCus ? 1 : 2;
 }
 
 }  // namespace
 
-// Tile choice: the LDS-DMA kernel (128 x 256 tiles) from three quarters of
-// a block per CU (192 tiles) up, the generic kernel in its largest tile that
-// still gives one block per CU below that, else its smallest tile.  (At M =
-// 512, K = 4096, N = 14336, 224 tiles, the whole projection took 123 us with
-// the LDS-DMA kernel and 174 us with the generic 64 x 128 one.)
+// Tile choice: the LDS-DMA kernel (128 x 256 tiles) from half a block per
+// CU (128 tiles) up, the generic kernel in its largest tile that still gives
+// one block per CU below that, else its smallest tile.  Even with CUs left
+// idle the LDS-DMA kernel wins there: 512 x 4096 x 14336 (224 tiles) 123
+// against 174 us for the whole projection with the generic 64 x 128 tile;
+// 300 x 4096 x 14336 (168 tiles) 102 against 158 us, 1024 x 4096 x 4096
+// (128 tiles) 95 against 112 us ([N, K] weights: 96 against 140 us); the
+// same bits.
 hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, const uint16_t *w,
                        int64_t ldw, float *y, int64_t ldy, float *c_hi, float *c_lo, int64_t ldc,
                        int64_t M, int64_t N, int64_t K, bool a_zero_padded, hipStream_t stream,
                        const float *bias, bool w_nk, bool geglu_rmw)
 {
     GemmArgs g{a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K, bias, geglu_rmw ? 1 : 0, 1, nullptr, 0};
-    if (tiles_of<TileLarge>(M, N) >= kCus * 3 / 4 && !geglu_rmw) {
+    if (tiles_of<TileLarge>(M, N) >= kCus / 2 && !geglu_rmw) {
         const hipError_t e = launch_gemm_dma(a_hi, a_lo, lda, w, ldw, y, ldy, c_hi, c_lo, ldc, M, N, K,
                                              a_zero_padded, stream, bias, w_nk);
         if (e != hipErrorNotSupported) return e;

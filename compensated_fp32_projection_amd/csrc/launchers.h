@@ -74,9 +74,9 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
                            const float *bias = nullptr, bool w_nk = false, int64_t kchunks = 1,
                            float *part = nullptr, int64_t n_pad = 0);
 
-// Split K on grids too small for the GPU: for 8 < M <= 64 fewer than 128
-// output tiles of 128 x 256, above that fewer than 192 (then only where the
-// chunks bring the grid to at least 192 blocks).  K is cut into 64-deep
+// Split K on grids too small for the GPU (fewer than 128 output tiles of
+// 128 x 256; above 64 rows only where the chunks bring the grid to at least
+// 192 blocks).  K is cut into 64-deep
 // units, dealt in order to `chunks` chunks as evenly as possible (at least 4
 // units each; chunks x tiles about 256, a multiple of 8 where one is within
 // reach; partial sums at most a quarter of W's bytes up to 64 rows, at most

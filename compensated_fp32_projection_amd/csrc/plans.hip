@@ -53,8 +53,8 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
 {
     GemmSplitPlan p{1, 0, 0};
     // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
-    // 35-52 us.  Above 64 rows the grid of 128 x 256 tiles must stay below
-    // the LDS-DMA kernel's own threshold (192 tiles), the chunks must bring
+    // 35-52 us.  Above 64 rows too the grid must stay below 128 tiles of
+    // 128 x 256 (where the LDS-DMA kernel takes over), the chunks must bring
     // it to at least 192 blocks, and the partial sums may take up to W's
     // bytes and 56 MiB: x W at 96 / 128 / 192 / 256 x 4096 x 14336 went from
     // 76.6 / 82.2 / 92.1 / 102.6 us (generic 32 x 128 tile) to 56.1 / 64.6 /
@@ -68,7 +68,7 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     if (M <= kGemvMaxRows || N <= 0 || K <= 0 || K % 8) return p;
     if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
     const int64_t tiles = ((M + kTileRows - 1) / kTileRows) * ((N + kTileCols - 1) / kTileCols);
-    if (tiles >= (M <= kSmallRows ? 128 : 192)) return p;
+    if (tiles >= 128) return p;
     int64_t c = 256 / tiles;
     for (int64_t cc = c; cc >= 1 && cc > c - 8; --cc)
         if ((cc * tiles) % 8 == 0) {

@@ -190,13 +190,13 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         least 128 output tiles of 128 x 256 and K % 4 == 0, ldx % 4 == 0,
  *         ldw % 8 == 0, x and w 16-byte aligned, one GEMM launch that splits
  *         x on the way into LDS (the workspace is then not touched; both give
- *         identical bits); or, on small grids with K % 8 == 0 (M <= 64
- *         with fewer than 128 tiles; above, fewer than 192 tiles where K is
- *         long enough to give each of at least 192 blocks four 64-deep
- *         units, with the partial sums within W's bytes and 56 MiB), the
+ *         identical bits); or, on small grids with K % 8 == 0 (fewer than
+ *         128 tiles; above 64 rows only where K is long enough to give each
+ *         of at least 192 blocks four 64-deep units, with the partial sums
+ *         within W's bytes and 56 MiB), the
  *         split, a GEMM over chunks of K writing FP32 partial sums into the
  *         workspace, and a merge dispatch (three launches); or,
- *         on grids the GEMM runs in 32 x 128 tiles (fewer than 192 tiles of
+ *         on grids the GEMM runs in 32 x 128 tiles (fewer than 128 tiles of
  *         128 x 256 and fewer than 256 of 64 x 128) with ldx % 4 == 0,
  *         ldw % 8 == 0 and x, w 16-byte aligned, one GEMM launch that splits
  *         x in registers as it loads it (the workspace is then not touched;

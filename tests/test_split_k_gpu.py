@@ -1,7 +1,6 @@
 """GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
-(8 < M <= 64, fewer than 128 output tiles of 128 x 256; above 64 rows,
-fewer than 192 tiles where K gives at least 192 blocks of four 64-deep
-units):
+(fewer than 128 output tiles of 128 x 256; above 64 rows only where K
+gives at least 192 blocks of four 64-deep units):
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
     units, each chunk's C_hi, C_lo go to FP32 partial sums, and a merge
     dispatch adds them in chunk order and merges once.  The plan depends on

@@ -92,9 +92,6 @@ size_t gemm_region_bytes(int64_t M, int64_t N, int64_t K, bool w_kn)
     return gemm_path > small_m ? gemm_path : small_m;
 }
 
-// Largest grid of the in-block split-K kernel (see ksplit_route).
-constexpr int64_t kKsplitMaxBlocks = 512;
-
 // Whether the projection takes the small-grid kernel (gemm_ksplit.hip) when
 // its operands allow it; M > kGemvMaxRows, K > 0.  Its grid must fit the
 // GPU at once (two blocks per CU: at most 512 blocks).
@@ -110,7 +107,7 @@ constexpr int64_t kKsplitMaxBlocks = 512;
 //    (512 x 768 x 2304: 21 -> 23 us; 512 x 4096 x 4096: 81 -> 90 us).
 bool ksplit_route(int64_t M, int64_t N, int64_t K, bool nk)
 {
-    if (cfp32::ksplit_blocks(M, N) > kKsplitMaxBlocks) return false;
+    if (cfp32::ksplit_blocks(M, N) > cfp32::kKsplitMaxBlocks) return false;
     if (nk && M <= cfp32::kGemvMaxRowsNK) return false;
     if (!nk && M <= cfp32::kGemvMaxRowsKN) {
         const cfp32::GemvPlan p = cfp32::gemv_plan(M, N, K);

@@ -21,8 +21,10 @@ hipError_t launch_merge(const float *c_hi, const float *c_lo, int64_t ldc, float
 // merge (+ bias) into y; W [K, N], or [N, K] with w_nk.  hipErrorNotSupported
 // (nothing enqueued) unless K % 8 == 0, ldx % 4 == 0, ldw % 8 == 0, x and w
 // 16-byte aligned and the byte offsets fit 31 bits.  ksplit_blocks: its
-// grid (one block per 32 x 64 output tile).
+// grid (one block per 32 x 64 output tile); it runs where that grid fits
+// the GPU at once (two blocks per CU: at most kKsplitMaxBlocks).
 constexpr int kKsplitTileM = 32, kKsplitTileN = 64;
+constexpr int64_t kKsplitMaxBlocks = 512;
 hipError_t launch_gemm_ksplit(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                               int64_t M, int64_t N, int64_t K, hipStream_t stream, const float *bias, bool w_nk);
 int64_t ksplit_blocks(int64_t M, int64_t N);  // plans.hip
@@ -76,9 +78,9 @@ hipError_t launch_gemm_dma(const uint16_t *a_hi, const uint16_t *a_lo, int64_t l
 
 // Split K on grids too small for the GPU (fewer than 128 output tiles of
 // 128 x 256; above 64 rows only where the chunks bring the grid to at least
-// 192 blocks).  K is cut into 64-deep
-// units, dealt in order to `chunks` chunks as evenly as possible (at least 4
-// units each; chunks x tiles about 256, a multiple of 8 where one is within
+// 128 blocks, 192 where the small-grid kernel could run it).  K is cut into
+// 64-deep units, dealt in order to `chunks` chunks as evenly as possible (at
+// least 4 units each; chunks x tiles about 256, a multiple of 8 where one is within
 // reach; partial sums at most a quarter of W's bytes up to 64 rows, at most
 // W's bytes and 56 MiB above); each chunk's C_hi, C_lo go to FP32
 // partial sums ([chunks][M][2][n_pad], workspace_bytes in all) that a merge

@@ -55,15 +55,16 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     // M <= 64: at 1 x 4096 x 14336 split K cuts M = 9..64 from 72-74 us to
     // 35-52 us.  Above 64 rows too the grid must stay below 128 tiles of
     // 128 x 256 (where the LDS-DMA kernel takes over), the chunks must bring
-    // it to at least 192 blocks, and the partial sums may take up to W's
+    // it to at least 128 blocks (192 where the small-grid kernel could run
+    // it instead), and the partial sums may take up to W's
     // bytes and 56 MiB: x W at 96 / 128 / 192 / 256 x 4096 x 14336 went from
     // 76.6 / 82.2 / 92.1 / 102.6 us (generic 32 x 128 tile) to 56.1 / 64.6 /
-    // 75.2 / 89.2 us, 128 x 8192 x 14336 from 159 to 97 us; where K per
+    // 75.2 / 89.2 us, 128 x 8192 x 14336 from 159 to 97 us, 300 / 512 x
+    // 4096 x 4096 (144 / 128 blocks) from 62 / 80 to 48 / 63 us; where K per
     // chunk is short (2048 x 1024 x 2048: 39 -> 55 us; 1024^3: 20 -> 33 us)
-    // or the blocks stay few (96 x 4096 x 4096: 28 -> 39 us against the
-    // small-grid kernel) it lost, which the conditions keep out.
+    // it lost, which the conditions keep out.
     constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kSmallRows = 64;
-    constexpr int64_t kMinBlocksWide = 192;
+    constexpr int64_t kMinBlocksWide = 128, kMinBlocksKsplit = 192;
     constexpr int64_t kMaxPartBytesWide = (int64_t)56 << 20;
     if (M <= kGemvMaxRows || N <= 0 || K <= 0 || K % 8) return p;
     if (M > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return p;
@@ -87,7 +88,11 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
         if (c > K / (4 * M)) c = K / (4 * M);
         const int64_t cap = kMaxPartBytesWide / (M * 2 * n_pad * (int64_t)sizeof(float));
         if (c > cap) c = cap;
-        if (c * tiles < kMinBlocksWide) return p;
+        // Where the small-grid kernel takes the grid (at most
+        // kKsplitMaxBlocks tiles of 32 x 64) it wins below 192 blocks (96 x
+        // 4096 x 4096: 28 us there, 39 us split in 160 blocks).
+        const int64_t min_blocks = ksplit_blocks(M, N) <= kKsplitMaxBlocks ? kMinBlocksKsplit : kMinBlocksWide;
+        if (c * tiles < min_blocks) return p;
     }
     if (c < 2) return p;
     p.chunks = c;

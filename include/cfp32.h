@@ -192,7 +192,9 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         x on the way into LDS (the workspace is then not touched; both give
  *         identical bits); or, on small grids with K % 8 == 0 (fewer than
  *         128 tiles; above 64 rows only where K is long enough to give each
- *         of at least 192 blocks four 64-deep units, with the partial sums
+ *         of at least 128 blocks (192 where the one-launch small-grid
+ *         path below could run the grid) four 64-deep units, with the
+ *         partial sums
  *         within W's bytes and 56 MiB), the
  *         split, a GEMM over chunks of K writing FP32 partial sums into the
  *         workspace, and a merge dispatch (three launches); or,

@@ -1,6 +1,7 @@
 """GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
 (fewer than 128 output tiles of 128 x 256; above 64 rows only where K
-gives at least 192 blocks of four 64-deep units):
+gives at least 128 blocks of four 64-deep units, 192 where the small-grid
+kernel could run the grid):
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
     units, each chunk's C_hi, C_lo go to FP32 partial sums, and a merge
     dispatch adds them in chunk order and merges once.  The plan depends on
@@ -130,8 +131,8 @@ def test_bias_is_one_addition(M, K, N, layout):
 
 # (M, K, N) above 64 rows: the batched FFN shape (four chunks), ragged M, N
 # and a ragged last unit of K, three chunks with 192 blocks, ragged M with
-# many chunks.
-WIDE_SPLIT = [(96, 4096, 14336), (200, 4000, 10000), (256, 4096, 8192), (130, 8192, 2056)]
+# many chunks, ragged M with three chunks and 144 blocks.
+WIDE_SPLIT = [(96, 4096, 14336), (200, 4000, 10000), (256, 4096, 8192), (130, 8192, 2056), (300, 4096, 4096)]
 
 
 @pytest.mark.parametrize("M,K,N", WIDE_SPLIT)

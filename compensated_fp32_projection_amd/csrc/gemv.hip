@@ -35,9 +35,10 @@
 // Every summation order is fixed, so results are identical from run to run.
 // W that is not 16-byte aligned with ldw % 8 == 0 (or too large for 32-bit
 // buffer offsets) goes through gemv_generic_kernel instead: one launch, a
-// block per 64 columns and all of K, element loads, FP32 FMAs on the vector
-// unit (an FP16 x FP16 product is exact in FP32, so fusing it into the
-// accumulation rounds once, as the matrix unit does).
+// block per 64 columns and all of K, W rows read at any 2-byte offset
+// (batched dword loads and funnel shifts), FP32 FMAs on the vector unit (an
+// FP16 x FP16 product is exact in FP32, so fusing it into the accumulation
+// rounds once, as the matrix unit does).
 #include <climits>
 #include <type_traits>
 
@@ -599,12 +600,24 @@ __global__ __launch_bounds__(256) void gemv_geglu_merge_kernel(const float *__re
 }
 
 // Fallback for W that is not 16-byte aligned or too large for 32-bit buffer
-// offsets: a block per 64 columns and all of K, element loads, the same
-// fixed-order reduction inside the block, one launch, no workspace.
+// offsets: a block per 64 columns and all of K, a thread per 8 columns and
+// every 64th row, the same fixed-order reduction inside the block, one
+// launch, no workspace.
+//   FAST (W within 31-bit byte offsets, ldw >= 16): rows 0 .. K - 2 come in
+//   batches of kGenericU rows per thread, all of a batch's loads issued
+//   before any is used.  The 8 columns at any even byte offset lie in the 20
+//   bytes from the dword below it (a 16-byte and a 4-byte buffer load), and
+//   a funnel shift by 0 or 16 bits picks them out; for those rows the 20
+//   bytes stay inside W (the next row follows), and columns past N only
+//   feed sums that are never stored.  The last row, and every row without
+//   FAST, is read by load_row8 (dwords, or elements at the row's end).
+//   Each thread adds its rows in increasing k either way: the same bits.
 constexpr int kGenericThreads = 512;
 constexpr int kGenericNB = 64;
+constexpr int kGenericU = 8;  // rows per batch up to 4 rows of x (4 beyond; 16 measured no faster)
+constexpr int kGenericNoOffset = 0x7FFFFFC0;  // a load here (and 16 bytes on) reads zero
 
-template <int MR>
+template <int MR, bool FAST>
 __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const float *__restrict__ x, int64_t ldx,
                                                                        const uint16_t *__restrict__ w, int64_t ldw,
                                                                        float *__restrict__ y, int64_t ldy,
@@ -628,16 +641,16 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
 #pragma unroll
         for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
 
-    for (int64_t k = kl; k < K; k += KL) {
-        const uint4 wv = load_row8<false>(w + k * ldw, n, N);
-        const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+    // One row: its 8 weights (FP16 bits, two per dword) times the split of
+    // x[m][k] for every row m of x, into the sums.
+    auto add_row = [&](const uint32_t (&d)[4], const float (&xv)[MR]) __attribute__((always_inline)) {
         float wf[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) wf[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             _Float16 h16, l16;
-            split_value(x[m * ldx + k], h16, l16);
+            split_value(xv[m], h16, l16);
             const float h = (float)h16, l = (float)l16;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -645,6 +658,63 @@ __global__ __launch_bounds__(kGenericThreads) void gemv_generic_kernel(const flo
                 sl[m][e] = __builtin_fmaf(l, wf[e], sl[m][e]);
             }
         }
+    };
+
+    int64_t k = kl;
+    if constexpr (FAST) {
+        const uintptr_t wa = reinterpret_cast<uintptr_t>(w);
+        const int delta = (int)(wa & 3);  // W may start at any even byte
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>(wa - (uintptr_t)delta), 0, (int)(delta + ((K - 1) * ldw + N) * 2), kBufferWord3);
+        const int64_t kfast = K - 1;
+        const bool col_ok = n < N;
+        constexpr int U = MR <= 4 ? kGenericU : kGenericU / 2;
+        for (; k < kfast; k += (int64_t)KL * U) {
+            uint32_t q[U][5];
+            int sft[U];
+            float xv[U][MR];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t kk = k + (int64_t)KL * u;
+                const bool ok = kk < kfast;
+                const int off = ok && col_ok ? (int)(delta + (kk * ldw + n) * 2) : kGenericNoOffset;
+                const int a = off & ~3;
+                sft[u] = (off & 2) << 3;
+                const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, a, 0, 0));
+                q[u][0] = v.x;
+                q[u][1] = v.y;
+                q[u][2] = v.z;
+                q[u][3] = v.w;
+                q[u][4] = __builtin_amdgcn_raw_buffer_load_b32(rs, a + 16, 0, 0);
+                // x is read at a valid row either way (no branch around the
+                // loads) and the value dropped past the batches' rows.
+                const int64_t kx = ok ? kk : kl;
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const float v = x[m * ldx + kx];
+                    xv[u][m] = ok ? v : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (k + (int64_t)KL * u >= kfast) break;
+                const uint32_t d[4] = {__builtin_amdgcn_alignbit(q[u][1], q[u][0], sft[u]),
+                                       __builtin_amdgcn_alignbit(q[u][2], q[u][1], sft[u]),
+                                       __builtin_amdgcn_alignbit(q[u][3], q[u][2], sft[u]),
+                                       __builtin_amdgcn_alignbit(q[u][4], q[u][3], sft[u])};
+                add_row(d, xv[u]);
+            }
+        }
+        // The first row of this thread past the batches (row K - 1 or none).
+        if (kl < kfast) k = kl + (kfast - kl + KL - 1) / KL * KL;
+    }
+    for (; k < K; k += KL) {
+        const uint4 wv = load_row8<false>(w + k * ldw, n, N);
+        const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+        float xv[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) xv[m] = x[m * ldx + k];
+        add_row(d, xv);
     }
     // Butterfly over the k-lanes of this wave (lanes c, c+CH, c+2CH, ...).
 #pragma unroll
@@ -1034,8 +1104,16 @@ hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_
 {
     const int64_t blocks = (N + kGenericNB - 1) / kGenericNB;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    gemv_generic_kernel<MR><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(x, ldx, w, ldw, y, ldy, N, K,
-                                                                                    bias, geglu_rmw ? 1 : 0);
+    // FAST: every byte offset into W (at most 2 + 2 ((K - 1) ldw + N) plus
+    // 20) stays below the kernel's zero-read offset.
+    constexpr int64_t kLimit = kGenericNoOffset - (1 << 20);
+    const bool fast = K >= 1 && ldw >= 16 && 2 + 2 * ((K - 1) * ldw + N) < kLimit;
+    if (fast)
+        gemv_generic_kernel<MR, true><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(
+            x, ldx, w, ldw, y, ldy, N, K, bias, geglu_rmw ? 1 : 0);
+    else
+        gemv_generic_kernel<MR, false><<<dim3((unsigned)blocks), kGenericThreads, 0, stream>>>(
+            x, ldx, w, ldw, y, ldy, N, K, bias, geglu_rmw ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -278,7 +278,9 @@ def test_linear_small_m_edges(M):
     """M = 1..8 take the small-M path, M = 9 the split + GEMM path; ragged N
     and K, padded leading dimensions, and weights that do (ldw % 8 == 0,
     16-byte aligned: chunked products + merge dispatch) and do not (one
-    generic kernel) allow 16-byte loads."""
+    generic kernel: batched 16 + 4-byte loads and funnel shifts when
+    ldw >= 16, the last row and narrower rows in dwords or elements)
+    allow 16-byte loads."""
     cases = [  # N, K, pointer offset of W in elements, extra ldw padding
         (777, 1000, 0, 7),    # aligned, ragged last tile and last chunk
         (777, 1000, 0, 0),    # ldw % 8 != 0
@@ -289,6 +291,9 @@ def test_linear_small_m_edges(M):
         (2048, 3000, 8, 0),   # aligned pointer offset, several tiles
         (512, 1, 0, 0),       # one row of W
         (140000, 100, 0, 0),  # more than 256 column tiles: one chunk, merged in place
+        (13, 1, 1, 4),        # unaligned, ldw >= 16, one row of W (only the last-row loads)
+        (13, 2, 1, 4),        # unaligned, two rows: one batched row, then the last
+        (600, 200, 3, 0),     # W at a 6-byte offset, ldw odd, K past three 64-row rounds
     ]
     for N, K, w_off, w_ld_pad in cases:
         A, W = workloads.random_case(M * 1000 + N + K, M, K, N, a_scale=100.0)

@@ -1039,6 +1039,8 @@ __global__ __launch_bounds__(64 * kNkWaves) void gemv_nk_kernel(const float *__r
 
 // [N, K] fallback for any alignment and K: a wave per output column, lanes
 // striding K, FP32 FMAs, a fixed-order butterfly over the wave.
+constexpr int kNkGenericU = 8;  // elements per lane in flight
+
 template <int MR>
 __global__ __launch_bounds__(256) void gemv_nk_generic_kernel(const float *__restrict__ x, int64_t ldx,
                                                               const uint16_t *__restrict__ w, int64_t ldw,
@@ -1051,14 +1053,36 @@ __global__ __launch_bounds__(256) void gemv_nk_generic_kernel(const float *__res
     float sh[MR], sl[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) sh[m] = 0.0f, sl[m] = 0.0f;
-    for (int64_t k = lane; k < K; k += 64) {
-        const float wf = half_bits_to_float(w[n * ldw + k]);
+    // Batches of kNkGenericU elements per lane, all loads of a batch issued
+    // before any is used (past K a lane reloads its batch's first element and
+    // drops it); each lane still adds its elements in increasing k.
+    const uint16_t *wr = w + n * ldw;
+    for (int64_t k = lane; k < K; k += 64 * kNkGenericU) {
+        uint32_t wb[kNkGenericU];
+        float xv[kNkGenericU][MR];
 #pragma unroll
-        for (int m = 0; m < MR; ++m) {
-            _Float16 h16, l16;
-            split_value(x[m * ldx + k], h16, l16);
-            sh[m] = __builtin_fmaf((float)h16, wf, sh[m]);
-            sl[m] = __builtin_fmaf((float)l16, wf, sl[m]);
+        for (int u = 0; u < kNkGenericU; ++u) {
+            const int64_t kk = k + 64 * u;
+            const int64_t kc = kk < K ? kk : k;
+            wb[u] = wr[kc];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) xv[u][m] = x[m * ldx + kc];
+        }
+        // Every product is formed and a select keeps or drops it: with a
+        // branch the compiler moves each load down to its use.
+#pragma unroll
+        for (int u = 0; u < kNkGenericU; ++u) {
+            const bool ok = k + 64 * u < K;
+            const float wf = half_bits_to_float(wb[u]);
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                _Float16 h16, l16;
+                split_value(xv[u][m], h16, l16);
+                const float th = __builtin_fmaf((float)h16, wf, sh[m]);
+                const float tl = __builtin_fmaf((float)l16, wf, sl[m]);
+                sh[m] = ok ? th : sh[m];
+                sl[m] = ok ? tl : sl[m];
+            }
         }
     }
 #pragma unroll

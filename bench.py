@@ -367,8 +367,8 @@ def summarize_counters(fetch_csv, write_csv, out_path, command):
 
 GEMV_SUMMARY = os.path.join(ROOT, "profiles", "decode_gemv_1x4096x14336_counters.txt")
 GEMV_PRODUCT_KERNEL = "gemv_valu_kernel<1>"  # the M = 1 product dispatch
-GEMV_MERGE_KERNEL = "gemv_merge4_kernel"
-GEMV_GRID = 14336 // 4                       # threads of the M = 1 merge dispatch (4 outputs each)
+GEMV_MERGE_KERNEL = "gemv_merge_kernel<64>"  # the M = 1 merge dispatch
+GEMV_GRID = 14336                            # its threads (one output each)
 
 
 def gemv_source_hash() -> str:

@@ -27,10 +27,11 @@
 //     workspace, or, when K is a single chunk, merges and writes y itself
 //     (no second dispatch).  For M <= 2, gemv_valu_kernel runs the same
 //     chunks with FP32 FMAs on the vector unit and deeper load queues.
-//  2. gemv_merge4_kernel (gemv_merge_kernel where 16-byte loads of the
-//     partial sums are not possible) -- for every output, sums the chunk
-//     partials of C_hi and of C_lo in chunk order, then merges
-//     y = C_hi + C_lo / 1024.  The split-K GEMM path uses it too.
+//  2. gemv_merge4_kernel (four outputs per thread), or gemv_merge_kernel
+//     (one: for small outputs, in 64-thread blocks, and where 16-byte loads
+//     of the partial sums are not possible) -- for every output, sums the
+//     chunk partials of C_hi and of C_lo in chunk order, then merges
+//     y = C_hi + C_lo / 1024.  The split-K GEMM path uses them too.
 //
 // Every summation order is fixed, so results are identical from run to run.
 // W that is not 16-byte aligned with ldw % 8 == 0 (or too large for 32-bit
@@ -467,12 +468,13 @@ hipError_t launch_product(const GemvArgs &g, int64_t blocks, hipStream_t stream)
 // chunks are issued before the first add, one memory latency per batch.
 constexpr int kMergeBatch = 16;
 
-__global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict__ part, int64_t n_pad,
+template <int TB>
+__global__ __launch_bounds__(TB) void gemv_merge_kernel(const float *__restrict__ part, int64_t n_pad,
                                                          int64_t chunks, int M, int64_t N,
                                                          float *__restrict__ y, int64_t ldy,
                                                          const float *__restrict__ bias)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * TB + threadIdx.x;
     if (i >= (int64_t)M * N) return;
     const int m = (int)(i / N);
     const int64_t n = i % N;
@@ -504,17 +506,18 @@ __global__ __launch_bounds__(256) void gemv_merge_kernel(const float *__restrict
 // the partial sums (n_pad is a multiple of 4, the partial sums 16-byte
 // aligned), a quarter of the load instructions for the same bytes.  Each
 // column is summed exactly as above (from +0, chunks in order).  VY: rows of
-// y take 16-byte stores (ldy % 4 == 0, y 16-byte aligned).
+// y take 16-byte stores (ldy % 4 == 0, y 16-byte aligned).  TB threads
+// per block: 64 where 256 would leave most CUs without a block.
 constexpr int kMergeBatch4 = 8;
 
-template <bool VY>
-__global__ __launch_bounds__(256) void gemv_merge4_kernel(const float *__restrict__ part, int64_t n_pad,
+template <bool VY, int TB>
+__global__ __launch_bounds__(TB) void gemv_merge4_kernel(const float *__restrict__ part, int64_t n_pad,
                                                           int64_t chunks, int M, int64_t N,
                                                           float *__restrict__ y, int64_t ldy,
                                                           const float *__restrict__ bias)
 {
     const int64_t groups = (N + 3) / 4;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * TB + threadIdx.x;
     if (i >= (int64_t)M * groups) return;
     const int m = (int)(i / groups);
     const int64_t n = 4 * (i % groups);
@@ -1159,20 +1162,38 @@ hipError_t launch_partial_merge(const float *part, int64_t n_pad, int64_t chunks
                                 int64_t ldy, const float *bias, hipStream_t stream)
 {
     const auto al16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    // Blocks of 64 threads while 256 would leave most CUs without one, and
+    // one output per thread up to 256 such blocks (1 x 4096 x 4096 decode:
+    // 16.8 -> 13.1 us; 1 x 4096 x 14336: 22.9 -> 22.1 us).  Every output is
+    // summed the same way in each form: the same bits.
+    const int64_t outs = M * N;
+    if (M <= 0x7FFFFFFF && outs <= 256 * 64) {
+        gemv_merge_kernel<64><<<dim3((unsigned)((outs + 63) / 64)), 64, 0, stream>>>(part, n_pad, chunks, (int)M, N,
+                                                                                     y, ldy, bias);
+        return hipGetLastError();
+    }
     if (n_pad % 4 == 0 && al16(part)) {
         const int64_t threads = M * ((N + 3) / 4);
         if (M > 0x7FFFFFFF || (threads + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        const dim3 grid((unsigned)((threads + 255) / 256));
-        if (ldy % 4 == 0 && al16(y))
-            gemv_merge4_kernel<true><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
-        else
-            gemv_merge4_kernel<false><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+        const bool vy = ldy % 4 == 0 && al16(y);
+        if (threads < 256 * 256) {
+            const dim3 grid((unsigned)((threads + 63) / 64));
+            if (vy)
+                gemv_merge4_kernel<true, 64><<<grid, 64, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+            else
+                gemv_merge4_kernel<false, 64><<<grid, 64, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+        } else {
+            const dim3 grid((unsigned)((threads + 255) / 256));
+            if (vy)
+                gemv_merge4_kernel<true, 256><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+            else
+                gemv_merge4_kernel<false, 256><<<grid, 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y, ldy, bias);
+        }
         return hipGetLastError();
     }
-    const int64_t outs = M * N;
     if (M > 0x7FFFFFFF || (outs + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    gemv_merge_kernel<<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, n_pad, chunks, (int)M, N, y,
-                                                                                 ldy, bias);
+    gemv_merge_kernel<256><<<dim3((unsigned)((outs + 255) / 256)), 256, 0, stream>>>(part, n_pad, chunks, (int)M, N,
+                                                                                      y, ldy, bias);
     return hipGetLastError();
 }
 

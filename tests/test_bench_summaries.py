@@ -54,12 +54,12 @@ def traffic_files(tmp_path):
                       (3, GEMM, 1835008, "FETCH_SIZE", 2.0e6, 0, 1500),
                       (4, GEMM, 262144, "FETCH_SIZE", 9.0e9, 0, 200),
                       (5, "gemv_valu_kernel<1>(GemvArgs)", 229376, "FETCH_SIZE", 57344.0, 0, 20000),
-                      (6, "gemv_merge4_kernel<true>(float const*)", bench.GEMV_GRID, "FETCH_SIZE", 512.0, 0, 4000)])
+                      (6, "gemv_merge_kernel<64>(float const*)", bench.GEMV_GRID, "FETCH_SIZE", 512.0, 0, 4000)])
     write_csv(write, [(1, COPY, 131072, "WRITE_SIZE", CALIB_KIB, 0, 100),
                       (2, GEMM, 1835008, "WRITE_SIZE", 4.0e5, 0, 1500),
                       (3, GEMM, 1835008, "WRITE_SIZE", 6.0e5, 0, 1500),
                       (5, "gemv_valu_kernel<1>(GemvArgs)", 229376, "WRITE_SIZE", 896.0, 0, 20000),
-                      (6, "gemv_merge4_kernel<true>(float const*)", bench.GEMV_GRID, "WRITE_SIZE", 56.0, 0, 4000)])
+                      (6, "gemv_merge_kernel<64>(float const*)", bench.GEMV_GRID, "WRITE_SIZE", 56.0, 0, 4000)])
     return fetch, write
 
 

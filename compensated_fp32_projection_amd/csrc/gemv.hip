@@ -1125,6 +1125,190 @@ bool buffer_path_ok(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
            ((reinterpret_cast<uintptr_t>(x) & 3) == 0) && (K + 1) * ldw * 2 < kLimit && M * ldx * 4 < kLimit;
 }
 
+// W rows at any 2-byte offset (ldw >= 16, 31-bit offsets), up to 8 rows of
+// x, K cut into the chunks of gemv_plan: a block (4 waves) owns one
+// 512-column tile of one chunk.  Lane l owns columns 8 l .. 8 l + 7 of the
+// tile, so one wave instruction reads a 1 KiB piece of one row of W (the
+// pattern the chunked kernels stream fastest); wave v takes the chunk's
+// rows v, v + 4, v + 8, ... in batches whose loads are all issued before
+// any is used (a 16-byte and a 4-byte buffer load from the dword below the
+// piece, then funnel shifts by 0 or 16 bits, as in gemv_generic_kernel; row
+// K - 1 by load_row8).  The four waves' sums are added in wave order
+// through LDS and written as the chunk's partial sums ([chunk][m][hi, lo]
+// [n_pad]); the merge dispatch adds the chunks in order and merges.
+constexpr int kUcWaves = 4;
+constexpr int kUcCols = 512;
+
+template <int MR>
+__global__ __launch_bounds__(64 * kUcWaves) void gemv_unaligned_chunk_kernel(
+    const float *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w, int64_t ldw, float *__restrict__ part,
+    int64_t n_pad, int64_t N, int64_t K, int64_t chunks, int64_t ntiles)
+{
+    __shared__ float red[kUcWaves - 1][MR][2][8][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tile = (int64_t)blockIdx.x % ntiles;
+    const int64_t chunk = (int64_t)blockIdx.x / ntiles;
+    const int64_t n = tile * kUcCols + 8 * lane;
+    const int64_t k_begin = chunk * K / chunks, k_end = (chunk + 1) * K / chunks;
+
+    float sh[MR][8], sl[MR][8];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sh[m][e] = 0.0f, sl[m][e] = 0.0f;
+    auto add_row = [&](const uint32_t (&d)[4], const float (&xv)[MR]) __attribute__((always_inline)) {
+        float wf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wf[e] = half_bits_to_float((d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            _Float16 h16, l16;
+            split_value(xv[m], h16, l16);
+            const float h = (float)h16, l = (float)l16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sh[m][e] = __builtin_fmaf(h, wf[e], sh[m][e]);
+                sl[m][e] = __builtin_fmaf(l, wf[e], sl[m][e]);
+            }
+        }
+    };
+
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(w);
+    const int delta = (int)(wa & 3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(wa - (uintptr_t)delta), 0, (int)(delta + ((K - 1) * ldw + N) * 2), kBufferWord3);
+    const int64_t kf = k_end < K - 1 ? k_end : K - 1;  // rows before kf: batched loads
+    const bool col_ok = n < N;
+    // Rows per batch: 24 for one row of x (8 KiB of W in flight per wave;
+    // 1 x 4096 x 14335: 34 -> 31 us against 8), else as gemv_generic_kernel.
+    constexpr int U = MR == 1 ? 3 * kGenericU : MR <= 4 ? kGenericU : kGenericU / 2;
+    int64_t k = k_begin + wave;
+    for (; k < kf; k += (int64_t)kUcWaves * U) {
+        uint32_t q[U][5];
+        int sft[U];
+        float xv[U][MR];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kk = k + (int64_t)kUcWaves * u;
+            const bool ok = kk < kf;
+            const int off = ok && col_ok ? (int)(delta + (kk * ldw + n) * 2) : kGenericNoOffset;
+            const int a = off & ~3;
+            sft[u] = (off & 2) << 3;
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, a, 0, 0));
+            q[u][0] = v.x;
+            q[u][1] = v.y;
+            q[u][2] = v.z;
+            q[u][3] = v.w;
+            q[u][4] = __builtin_amdgcn_raw_buffer_load_b32(rs, a + 16, 0, 0);
+            const int64_t kx = ok ? kk : k;  // a valid row either way; the value is dropped
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float v = x[m * ldx + kx];
+                xv[u][m] = ok ? v : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (k + (int64_t)kUcWaves * u >= kf) break;
+            const uint32_t d[4] = {__builtin_amdgcn_alignbit(q[u][1], q[u][0], sft[u]),
+                                   __builtin_amdgcn_alignbit(q[u][2], q[u][1], sft[u]),
+                                   __builtin_amdgcn_alignbit(q[u][3], q[u][2], sft[u]),
+                                   __builtin_amdgcn_alignbit(q[u][4], q[u][3], sft[u])};
+            add_row(d, xv[u]);
+        }
+    }
+    // Row K - 1, in the last chunk, by the wave whose rows reach it.
+    const int64_t r0 = k_begin + wave;
+    if (r0 < kf) k = r0 + (kf - r0 + kUcWaves - 1) / kUcWaves * kUcWaves;
+    else k = r0;
+    for (; k < k_end; k += kUcWaves) {
+        const uint4 wv = load_row8<false>(w + k * ldw, n, N);
+        const uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+        float xv[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) xv[m] = x[m * ldx + k];
+        add_row(d, xv);
+    }
+
+    // Waves 1-3 hand their sums to wave 0, which adds them in wave order.
+    if (wave > 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                red[wave - 1][m][0][e][lane] = sh[m][e];
+                red[wave - 1][m][1][e][lane] = sl[m][e];
+            }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int v = 0; v < kUcWaves - 1; ++v)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sh[m][e] += red[v][m][0][e][lane];
+                sl[m][e] += red[v][m][1][e][lane];
+            }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        float *ph = part + ((chunk * MR + m) * 2) * n_pad + n;
+        const floatx4_t h0 = {sh[m][0], sh[m][1], sh[m][2], sh[m][3]}, h1 = {sh[m][4], sh[m][5], sh[m][6], sh[m][7]};
+        const floatx4_t l0 = {sl[m][0], sl[m][1], sl[m][2], sl[m][3]}, l1 = {sl[m][4], sl[m][5], sl[m][6], sl[m][7]};
+        __builtin_nontemporal_store(h0, reinterpret_cast<floatx4_t *>(ph));
+        __builtin_nontemporal_store(h1, reinterpret_cast<floatx4_t *>(ph + 4));
+        __builtin_nontemporal_store(l0, reinterpret_cast<floatx4_t *>(ph + n_pad));
+        __builtin_nontemporal_store(l1, reinterpret_cast<floatx4_t *>(ph + n_pad + 4));
+    }
+}
+
+// The chunked product (partial sums of plan p in `part`) when p cuts K in
+// at least two chunks, W fits the kernel's offsets, and either x has one
+// row or gemv_generic_kernel would run fewer than 128 blocks (N <= 8128);
+// else hipErrorNotSupported, nothing enqueued.  With more rows of x and
+// wider W the vector unit bounds both forms and gemv_generic_kernel's eight
+// waves per CU do better (4 x 4096 x 14335: 43 against 48 us; 4 x 14336 x
+// 4097: 112 against 59 us with 65 blocks).  The plain projection and the
+// GEGLU one take it under the same condition (the GEGLU plan is the plan of
+// all 2F columns), so both sum every column the same way.
+template <int MR>
+hipError_t launch_unaligned_product(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, int64_t N,
+                                    int64_t K, const GemvPlan &p, float *part, size_t part_bytes,
+                                    hipStream_t stream)
+{
+    static_assert(kUcCols == kTileN, "the plan's column tiles");
+    constexpr int64_t kLimit = kGenericNoOffset - (1 << 20);
+    if (p.chunks < 2 || !part || part_bytes < p.workspace_bytes || (reinterpret_cast<uintptr_t>(part) & 15) ||
+        K < 1 || ldw < 16 || 2 + 2 * ((K - 1) * ldw + N) >= kLimit)
+        return hipErrorNotSupported;
+    if (MR > 1 && (N + kGenericNB - 1) / kGenericNB >= 128) return hipErrorNotSupported;
+    const int64_t ntiles = tiles_of(N);
+    const int64_t blocks = ntiles * p.chunks;
+    if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
+    gemv_unaligned_chunk_kernel<MR><<<dim3((unsigned)blocks), 64 * kUcWaves, 0, stream>>>(
+        x, ldx, w, ldw, part, p.n_pad, N, K, p.chunks, ntiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_unaligned_product_m(int64_t M, const float *x, int64_t ldx, const uint16_t *w, int64_t ldw,
+                                      int64_t N, int64_t K, const GemvPlan &p, float *part, size_t part_bytes,
+                                      hipStream_t stream)
+{
+    switch (M) {
+    case 1: return launch_unaligned_product<1>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 2: return launch_unaligned_product<2>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 3: return launch_unaligned_product<3>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 4: return launch_unaligned_product<4>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 5: return launch_unaligned_product<5>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 6: return launch_unaligned_product<6>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 7: return launch_unaligned_product<7>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    case 8: return launch_unaligned_product<8>(x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+    }
+    return hipErrorNotSupported;
+}
+
 template <int MR>
 hipError_t launch_generic(const float *x, int64_t ldx, const uint16_t *w, int64_t ldw, float *y, int64_t ldy,
                           int64_t N, int64_t K, hipStream_t stream, const float *bias, bool geglu_rmw)
@@ -1214,6 +1398,16 @@ hipError_t launch_gemv(const float *x, int64_t ldx, const uint16_t *w, int64_t l
         return launch_partial_merge(part, p.n_pad, p.chunks, M, N, y, ldy, bias, stream);
     }
     if (M > kGemvMaxRows) return hipErrorNotSupported;  // the GEMM path takes it
+    if (!geglu_rmw) {
+        // W rows that do not allow 16-byte loads, K cut into chunks: the
+        // chunked product and the merge dispatch (1 x 4096 x 14335: 35 -> 24
+        // us), else one launch of gemv_generic_kernel below.
+        const hipError_t e = launch_unaligned_product_m(M, x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+        if (e != hipErrorNotSupported) {
+            if (e != hipSuccess) return e;
+            return launch_partial_merge(part, p.n_pad, p.chunks, M, N, y, ldy, bias, stream);
+        }
+    }
     switch (M) {
     case 1: return launch_generic<1>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
     case 2: return launch_generic<2>(x, ldx, w, ldw, y, ldy, N, K, stream, bias, geglu_rmw);
@@ -1237,13 +1431,23 @@ hipError_t launch_gemv_geglu(const float *x, int64_t ldx, const uint16_t *w, int
 {
     if (M < 1 || M > kGemvMaxRowsKN) return hipErrorInvalidValue;
     const GemvPlan p = gemv_geglu_plan(M, F, K);
-    if (p.chunks == 0 || !buffer_path_ok(x, ldx, w, ldw, M, K) || !part || part_bytes < p.workspace_bytes)
-        return hipErrorNotSupported;
     const int64_t N = 2 * F;
-    const int64_t blocks = tiles_of(N) * p.chunks;
-    if (blocks > 0x7FFFFFFF || (M * F + 255) / 256 > 0x7FFFFFFF) return hipErrorNotSupported;
-    GemvArgs g{x, ldx, w, ldw, part, nullptr, 0, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), nullptr, 1};
-    hipError_t e = launch_product(g, blocks, stream);
+    if (p.chunks == 0 || !part || part_bytes < p.workspace_bytes || (M * F + 255) / 256 > 0x7FFFFFFF)
+        return hipErrorNotSupported;
+    hipError_t e;
+    if (buffer_path_ok(x, ldx, w, ldw, M, K)) {
+        const int64_t blocks = tiles_of(N) * p.chunks;
+        if (blocks > 0x7FFFFFFF) return hipErrorNotSupported;
+        GemvArgs g{x, ldx, w, ldw, part, nullptr, 0, p.n_pad, M, N, K, p.stages, p.chunks, tiles_of(N), nullptr, 1};
+        e = launch_product(g, blocks, stream);
+    } else {
+        // W rows that do not allow 16-byte loads: the chunked product where
+        // the plain projection takes it (up to 8 rows), else the caller's
+        // two-pass fallback.
+        if (M > kGemvMaxRows) return hipErrorNotSupported;
+        e = launch_unaligned_product_m(M, x, ldx, w, ldw, N, K, p, part, part_bytes, stream);
+        if (e == hipErrorNotSupported) return e;
+    }
     if (e != hipSuccess) return e;
     gemv_geglu_merge_kernel<<<dim3((unsigned)((M * F + 255) / 256)), 256, 0, stream>>>(part, p.n_pad, p.chunks,
                                                                                         (int)M, F, out, ldo, bias);

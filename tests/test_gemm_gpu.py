@@ -277,10 +277,11 @@ def test_linear_decode_gemv_full():
 def test_linear_small_m_edges(M):
     """M = 1..8 take the small-M path, M = 9 the split + GEMM path; ragged N
     and K, padded leading dimensions, and weights that do (ldw % 8 == 0,
-    16-byte aligned: chunked products + merge dispatch) and do not (one
-    generic kernel: batched 16 + 4-byte loads and funnel shifts when
-    ldw >= 16, the last row and narrower rows in dwords or elements)
-    allow 16-byte loads."""
+    16-byte aligned: chunked products + merge dispatch) and do not allow
+    16-byte loads (batched 16 + 4-byte loads and funnel shifts when
+    ldw >= 16: in chunks with a merge dispatch at one row of x or narrow
+    W, else one strip kernel; the last row and narrower rows in dwords or
+    elements)."""
     cases = [  # N, K, pointer offset of W in elements, extra ldw padding
         (777, 1000, 0, 7),    # aligned, ragged last tile and last chunk
         (777, 1000, 0, 0),    # ldw % 8 != 0
@@ -294,6 +295,7 @@ def test_linear_small_m_edges(M):
         (13, 1, 1, 4),        # unaligned, ldw >= 16, one row of W (only the last-row loads)
         (13, 2, 1, 4),        # unaligned, two rows: one batched row, then the last
         (600, 200, 3, 0),     # W at a 6-byte offset, ldw odd, K past three 64-row rounds
+        (9000, 300, 1, 0),    # unaligned, wide: chunked at one row of x, one launch above
     ]
     for N, K, w_off, w_ld_pad in cases:
         A, W = workloads.random_case(M * 1000 + N + K, M, K, N, a_scale=100.0)

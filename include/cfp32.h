@@ -169,8 +169,11 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * M <= 8: a product kernel (split in registers, both products over row
  *         chunks of K, FP32 partial sums into the workspace), then a merge
  *         kernel that sums the chunks in order and merges (two launches).
- *         W that is not 16-byte aligned with ldw % 8 == 0 takes one fused
- *         kernel instead, which leaves the workspace untouched.
+ *         W that is not 16-byte aligned with ldw % 8 == 0 is read at its
+ *         2-byte offsets instead: with one row of x, or N <= 8128, by a
+ *         chunked product kernel with the same partial sums and merge;
+ *         otherwise (or when K is one chunk, or ldw < 16) by one fused
+ *         kernel over all of K that leaves the workspace untouched.
  * 8 < M <= 16 with W 16-byte aligned and ldw % 8 == 0: the same two
  *         launches, two groups of 8 rows of x sharing every W fragment.
  * M  > 8 with N not a multiple of 8 and W rows that do not allow 16-byte

@@ -4,7 +4,8 @@ device memory, its scratch in a fixed array the library holds per device.
 Through the C ABI, on two calls in a row with the second smaller than the
 first (the array keeps the first call's contents, which must not matter),
 its output equals cfp32_linear's with a workspace bit for bit, on each path:
-the small-M dispatches (partial sums in the array), split K over a small grid
+the small-M dispatches (partial sums in the array; also for W rows that do
+not allow 16-byte loads), split K over a small grid
 (planes and partial sums), split + GEMM (planes exactly filling the 64 MiB),
 the generic GEMM for unaligned shapes, split K above 64 rows, and, above 64
 rows, a problem whose planes would not fit, which runs the GEMM that splits
@@ -55,6 +56,7 @@ PAIRS = [
     ((64, 4096, 14336), (16, 2048, 3000)),     # split K (planes + partial sums); two groups of 8 rows
     ((8192, 4096, 14336), (333, 1000, 777)),   # planes of 128 MiB: split inside; then the generic GEMM
     ((256, 4096, 14336), (96, 4096, 14336)),   # split K above 64 rows (63 MB of planes and partial sums), twice
+    ((1, 4096, 14335), (3, 1000, 777)),        # W rows not 16-byte loadable: chunked partial sums, twice
 ]
 
 

@@ -108,6 +108,17 @@ __device__ __forceinline__ int w_slot(int kg, int n)
     return T::LDS_A + kg * T::BN + (n ^ ((n >> 3) & 7));
 }
 
+// The same for W given as [N, K]: the 8 granules of a column are stored
+// together (the 8 lanes that load a column's 128 bytes write one 128-byte
+// LDS row; in the layout above they all hit the same banks), their order
+// XOR-ed with bits 1-3 of n, so that the 16 consecutive columns a B
+// fragment read takes at one k-group fall in 16 different bank groups.
+template <class T>
+__device__ __forceinline__ int w_slot_nk(int kg, int n)
+{
+    return T::LDS_A + n * kKG + (kg ^ ((n >> 1) & 7));
+}
+
 // Offset that no buffer reaches: a raw buffer load at it returns zero and
 // touches no memory, whether or not the scalar offset enters the range check.
 constexpr int kNoOffset = 0x7FFFFFF0;
@@ -365,7 +376,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
 #pragma unroll
             for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
                 const int c = tid + kThreads * q;
-                s[w_slot<T>(c & 7, c >> 3)] = rw[q >> 3][q & 7];
+                s[w_slot_nk<T>(c & 7, c >> 3)] = rw[q >> 3][q & 7];
             }
             return;
         }
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int n = wn * T::WTN + j * 32 + (lane & 31);
-            f.bw[j] = __builtin_bit_cast(half8_t, s[w_slot<T>(kg, n)]);
+            f.bw[j] = __builtin_bit_cast(half8_t, s[WNK ? w_slot_nk<T>(kg, n) : w_slot<T>(kg, n)]);
         }
     };
     auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {

@@ -42,6 +42,9 @@ namespace cfp32 {
 
 namespace {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+
 constexpr int kThreads = 256;
 constexpr int kBK = 64;        // k per stage
 constexpr int kKG = kBK / 8;   // k-granules per stage
@@ -117,6 +120,17 @@ template <class T>
 __device__ __forceinline__ int w_slot_nk(int kg, int n)
 {
     return T::LDS_A + n * kKG + (kg ^ ((n >> 1) & 7));
+}
+
+// [K, N] W in the 128-column tiles: the stage's 64 rows as loaded (row k,
+// granule ng of 8 columns), the granule order XOR-ed with 4 (k % 4).  A
+// store instruction writes whole 256-byte rows; a transposed B read (rows
+// k .. k + 3 and k + 8 .. k + 11 at four granules) meets every bank group
+// twice, the least for its 512 bytes.
+template <class T>
+__device__ __forceinline__ int w_slot_kn(int k, int ng)
+{
+    return T::LDS_A + k * (T::BN / 8) + (ng ^ (4 * (k & 3)));
 }
 
 // Offset that no buffer reaches: a raw buffer load at it returns zero and
@@ -208,6 +222,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             }
     };
 
+    // [K, N] W in 128-column tiles: stored as loaded, B fragments by the
+    // gfx950 transposed LDS read (no register transpose).
+    constexpr bool kTR = !WNK && T::BN == 128;
     // Staging registers.  The 32 x 128 tile (plain accumulation, 16-byte
     // loads) keeps two sets, so that a stage's loads land in one set while
     // the previous stage's set is written to LDS; the others use set 0 only.
@@ -237,6 +254,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             const int c = tid + kThreads * q;
             const int64_t gn = n0 + (c >> 3);
             voff_wn[q] = gn < g.N ? (int)((gn * g.ldw + 8 * (c & 7)) * 2) : kNoOffset;
+        }
+    }
+    // kTR: granule q of every thread is stage row c / (BN / 8), 8 columns
+    // at (c % (BN / 8)) * 8, c = tid + kThreads q (whole 256-byte rows per
+    // 16 lanes); the stage adds its k0 rows as a scalar offset.
+    if constexpr (BUF && kTR) {
+#pragma unroll
+        for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+            const int c = tid + kThreads * q;
+            const int64_t gn = n0 + 8 * (c % (T::BN / 8));
+            voff_wn[q] = gn < g.N ? (int)(((int64_t)(c / (T::BN / 8)) * g.ldw + gn) * 2) : kNoOffset;
         }
     }
     if constexpr (BUF) {
@@ -279,6 +307,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             for (int q = 0; q < T::W_NK_CHUNKS; ++q)
                 rw[q >> 3][q & 7] =
                     __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_wn[q], so_k, 0));
+            return;
+        }
+        if constexpr (kTR) {
+            const int so_r = __builtin_amdgcn_readfirstlane((int)(k0 * g.ldw * 2));
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q)
+                rw[q >> 3][q & 7] =
+                    __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_wn[q], so_r, 0));
             return;
         }
 #pragma unroll
@@ -331,6 +367,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             }
             return;
         }
+        if constexpr (kTR) {
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+                const int c = tid + kThreads * q;
+                const int64_t gk = k0 + c / (T::BN / 8), gn = n0 + 8 * (c % (T::BN / 8));
+                rw[q >> 3][q & 7] = gk < klim ? load_row8<AL_W>(g.w + gk * g.ldw, gn, g.N) : make_uint4(0, 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
             const int b = tid + kThreads * j;
@@ -380,6 +425,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
             }
             return;
         }
+        if constexpr (kTR) {
+#pragma unroll
+            for (int q = 0; q < T::W_NK_CHUNKS; ++q) {
+                const int c = tid + kThreads * q;
+                s[w_slot_kn<T>(c / (T::BN / 8), c % (T::BN / 8))] = rw[q >> 3][q & 7];
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < T::W_ITERS; ++j) {
             const int b = tid + kThreads * j;
@@ -418,6 +471,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(T::BM 
         }
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
+            if constexpr (kTR) {
+                // Lanes in groups of 16: group G takes columns 16 (G % 2) ..
+                // + 15 at k = 16 ks + 8 (G / 2) .. + 7; lane i of a group
+                // addresses row (i / 4) + 4 h at columns 4 (i % 4) .. + 3, and
+                // the transposed read hands it column i at those four rows.
+                const int grp = lane >> 4, li = lane & 15;
+                const int c = wn * T::WTN + j * 32 + 16 * (grp & 1) + 4 * (li & 3);
+                short4_t t[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k = 16 * ks + 8 * (grp >> 1) + (li >> 2) + 4 * h;
+                    const int byte = w_slot_kn<T>(k, c >> 3) * 16 + (c & 7) * 2;
+                    t[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) short4_t *)((__attribute__((address_space(3))) char *)s + byte));
+                }
+                const short8_t v = {t[0][0], t[0][1], t[0][2], t[0][3], t[1][0], t[1][1], t[1][2], t[1][3]};
+                f.bw[j] = __builtin_bit_cast(half8_t, v);
+                continue;
+            }
             const int n = wn * T::WTN + j * 32 + (lane & 31);
             f.bw[j] = __builtin_bit_cast(half8_t, s[WNK ? w_slot_nk<T>(kg, n) : w_slot<T>(kg, n)]);
         }

@@ -669,19 +669,31 @@ int64_t tiles_of(int64_t M, int64_t N)
 
 constexpr int64_t kCus = 256;
 
+// Below the LDS-DMA kernel's grids, the 64 x 128 tile only where the
+// 32 x 128 tile would deal more than three tiles to each CU (2048 x 4096 x
+// 1792, 896 small tiles: 107 against 123 us); with its two register sets,
+// loads two stages ahead and the split in registers, the 32 x 128 tile won
+// up to there (1024 x 4096 x 2048: 85 -> 60 us, 2048 x 8192 x 1024: 168 ->
+// 110 us, 4096 x 2048 x 512: 60 -> 34 us, 3000 x 3000 x 1000 [N, K]: 85 ->
+// 77 us).
+bool medium_tile(int64_t M, int64_t N)
+{
+    return tiles_of<TileMedium>(M, N) >= kCus && tiles_of<TileSmall>(M, N) > 3 * kCus;
+}
+
 // The generic kernel's tile for an M x N output when the LDS-DMA kernel does
 // not run: 0 = 128 x 256, 1 = 64 x 128, 2 = 32 x 128 (see launch_gemm).
 int generic_tile(int64_t M, int64_t N)
 {
     if (tiles_of<TileLarge>(M, N) >= kCus / 2) return 0;
-    return tiles_of<TileMedium>(M, N) >= kCus ? 1 : 2;
+    return medium_tile(M, N) ? 1 : 2;
 }
 
 }  // namespace
 
 // Tile choice: the LDS-DMA kernel (128 x 256 tiles) from half a block per
-// CU (128 tiles) up, the generic kernel in its largest tile that still gives
-// one block per CU below that, else its smallest tile.  Even with CUs left
+// CU (128 tiles) up, below that the generic kernel's 32 x 128 tile, or its
+// 64 x 128 tile on the largest of those grids (medium_tile).  Even with CUs left
 // idle the LDS-DMA kernel wins there: 512 x 4096 x 14336 (224 tiles) 123
 // against 174 us for the whole projection with the generic 64 x 128 tile;
 // 300 x 4096 x 14336 (168 tiles) 102 against 158 us, 1024 x 4096 x 4096
@@ -699,7 +711,7 @@ hipError_t launch_gemm(const uint16_t *a_hi, const uint16_t *a_lo, int64_t lda, 
         if (e != hipErrorNotSupported) return e;
         return w_nk ? launch_tile<TileLarge, 0, true>(g, stream) : launch_tile<TileLarge>(g, stream);
     }
-    if (tiles_of<TileMedium>(M, N) >= kCus)
+    if (medium_tile(M, N))
         return w_nk ? launch_tile<TileMedium, 0, true>(g, stream) : launch_tile<TileMedium>(g, stream);
     return w_nk ? launch_tile<TileSmall, 0, true>(g, stream) : launch_tile<TileSmall>(g, stream);
 }

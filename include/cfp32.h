@@ -206,7 +206,8 @@ CFP32_API size_t cfp32_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
  *         split, a GEMM over chunks of K writing FP32 partial sums into the
  *         workspace, and a merge dispatch (three launches); or,
  *         on grids the GEMM runs in 32 x 128 tiles (fewer than 128 tiles of
- *         128 x 256 and fewer than 256 of 64 x 128) with ldx % 4 == 0,
+ *         128 x 256, and at most 768 of 32 x 128 or fewer than 256 of
+ *         64 x 128) with ldx % 4 == 0,
  *         ldw % 8 == 0 and x, w 16-byte aligned, one GEMM launch that splits
  *         x in registers as it loads it (the workspace is then not touched;
  *         the bits of the two launches).

@@ -22,12 +22,15 @@ pytestmark = pytest.mark.gpu
 
 
 def small_tile_grid(M, N):
-    """Grids the generic kernel runs in its 32 x 128 tile, with more than 512
-    small-grid tiles of 32 x 64 (fewer take the small-grid kernel)."""
+    """Grids the generic kernel runs in its 32 x 128 tile (fewer than 128
+    tiles of 128 x 256; at most 768 of 32 x 128 or fewer than 256 of
+    64 x 128), with more than 512 small-grid tiles of 32 x 64 (fewer take the
+    small-grid kernel)."""
     large = ((M + 127) // 128) * ((N + 255) // 256)
     medium = ((M + 63) // 64) * ((N + 127) // 128)
+    small = ((M + 31) // 32) * ((N + 127) // 128)
     ks = ((M + 31) // 32) * ((N + 63) // 64)
-    return large < 192 and medium < 256 and ks > 512
+    return large < 128 and (medium < 256 or small <= 768) and ks > 512
 
 
 def linear(A, W, layout=cf.W_KN, bias=None, ldx=None):
@@ -72,8 +75,9 @@ def two_launch(A, W):
 # (M, K, N): the QKV workload's shape; K = 776 (twelve 64-deep stages and a
 # ragged 8) with ragged M and N (N % 8 != 0: after the padded copy); K = 200
 # (three full stages and a ragged one: one stage ahead); a larger K; a wide,
-# short one.
-SHAPES = [(512, 768, 2304), (520, 776, 2300), (600, 200, 2000), (384, 2048, 3072), (320, 72, 4000)]
+# short one; a grid of 256 tiles of 64 x 128 that takes the 32 x 128 tile.
+SHAPES = [(512, 768, 2304), (520, 776, 2300), (600, 200, 2000), (384, 2048, 3072), (320, 72, 4000),
+          (1024, 1024, 2048)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)

@@ -101,10 +101,14 @@ size_t gemm_region_bytes(int64_t M, int64_t N, int64_t K, bool w_kn)
 //    us; 16 x 1024 x 1024: 13.9 -> 10.2 us; with K = 4096 (32 stages per
 //    wave) it lost (16 x 4096 x 1024: 16.4 -> 20.5 us).
 //  * [N, K] weights up to 32 rows: never (the small-M [N, K] dispatch).
-//  * Above: where K is not split across blocks.  96 x 4096 x 4096: 62 ->
-//    27 us; 256 x 4096 x 4096: 72 -> 46 us; 1024^3: 26 -> 21 us; beyond 512
-//    blocks its 32 x 64 tiles re-read x and W more than the large tiles do
-//    (512 x 768 x 2304: 21 -> 23 us; 512 x 4096 x 4096: 81 -> 90 us).
+//  * Above: where K is not split across blocks and the generic kernel's
+//    32 x 128 tiles would number fewer than 128 (half the CUs); from there
+//    that one-launch form is faster (256 x 4096 x 4096: 46 -> 35 us; 200 x
+//    1024 x 4096: 19 -> 13 us; 1024^3: 20 -> 13.4 us; 512 x 1024 x 1024:
+//    13.6 -> 12.3 us), below it this kernel (96 x 4096 x 4096: 26.6 against
+//    33.2 us; 128 x 2048 x 2048: 17.6 against 19.1 us; 333 x 1000 x 784:
+//    12.7 against 14.5 us).  Beyond 512 blocks its 32 x 64 tiles re-read x
+//    and W more than the large tiles do.
 bool ksplit_route(int64_t M, int64_t N, int64_t K, bool nk)
 {
     if (cfp32::ksplit_blocks(M, N) > cfp32::kKsplitMaxBlocks) return false;
@@ -113,7 +117,8 @@ bool ksplit_route(int64_t M, int64_t N, int64_t K, bool nk)
         const cfp32::GemvPlan p = cfp32::gemv_plan(M, N, K);
         return K <= 1024 && p.chunks * ((N + cfp32::kGemvTileN - 1) / cfp32::kGemvTileN) < 64;
     }
-    return cfp32::gemm_split_plan(M, N, K).chunks <= 1;
+    const int64_t small_tiles = ((M + 31) / 32) * ((N + 127) / 128);  // the generic kernel's 32 x 128 tiles
+    return small_tiles < 128 && cfp32::gemm_split_plan(M, N, K).chunks <= 1;
 }
 
 // GEGLU (M > kGemvMaxRows): as cfp32_linear_ex over the [K, 2F] weight, the

@@ -2,7 +2,8 @@
 waves of each 32 x 64 output tile, x split in registers, one launch.
 
 cfp32_linear takes it for projections that do not split K across blocks and
-whose 32 x 64 tiles fit the GPU at once (at most 512 blocks).  Its summation
+whose 32 x 64 tiles fit the GPU at once (at most 512 blocks), where the
+generic kernel's 32 x 128 tiles would number fewer than 128.  Its summation
 order differs from the K-sequential kernels', so its bits are its own; the
 checks are those of every path (compensated-FP32 paragraph of the laya.cpp
 Vulkan guide): every element within 1e-5 * sum |a w| of the FP64 reference,
@@ -46,18 +47,21 @@ def run(A, W, layout=cf.W_KN, bias=None, stream=None):
 
 
 def takes_ksplit(M, N, K):
-    """At most 512 tiles of 32 x 64, K % 8 == 0, and no split of K across
-    blocks (that needs M <= 64 and at least four 64-deep units per chunk)."""
+    """At most 512 tiles of 32 x 64 and fewer than 128 of 32 x 128 (from
+    there the generic kernel's 32 x 128 tile), K % 8 == 0, and no split of K
+    across blocks (that needs M <= 64 and at least four 64-deep units per
+    chunk)."""
     tiles = ((M + 31) // 32) * ((N + 63) // 64)
-    return tiles <= 512 and K % 8 == 0 and (M > 64 or K < 512)
+    small = ((M + 31) // 32) * ((N + 127) // 128)
+    return tiles <= 512 and small < 128 and K % 8 == 0 and (M > 64 or K < 512)
 
 
-# (M, K, N): config 3's rows and K; several 128-row panels of a 4096 x 4096
-# weight; a cube; ragged M, N and a K that is not a whole number of 32-deep
-# stages (264 = 33 x 8); K below one stage; 40 rows with K too short to
-# split across blocks; one output column; a single column of tiles with
-# K = 4096.
-SHAPES = [(96, 4096, 4096), (256, 4096, 4096), (1024, 1024, 1024), (200, 2048, 3000), (65, 264, 130),
+# (M, K, N): 96 rows of a 4096 x 4096 weight; a square panel; a cube; the
+# unaligned workload's rows and K with N rounded to 8; ragged M, N and a K
+# that is not a whole number of 32-deep stages (264 = 33 x 8); K below one
+# stage; 40 rows with K too short to split across blocks; one output
+# column; a single column of tiles with K = 4096.
+SHAPES = [(96, 4096, 4096), (128, 2048, 2048), (512, 512, 512), (333, 1000, 784), (65, 264, 130),
           (100, 8, 72), (40, 40, 64), (130, 4096, 1), (512, 4096, 64)]
 
 

@@ -80,6 +80,13 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     if (c > units / kMinUnits) c = units / kMinUnits;
     const int64_t n_pad = (N + 63) / 64 * 64;
     if (M <= kSmallRows) {
+        // From 17 rows, no split where the generic kernel's 32 x 128 tiles
+        // alone give 192 or more blocks: that one-launch form walks all of K
+        // without partial sums (64 / 48 x 4096 x 14336: 45.1 / 42.0 -> 40.6 /
+        // 39.2 us; [N, K] 64 rows 45.4 -> 41.6 us); on smaller grids, or
+        // with long K, split K stays ahead (64 x 4096 x 4096: 26 us either
+        // way; 64 x 14336 x 4096: 52 against 94 us).
+        if (M > 16 && ((M + 31) / 32) * ((N + 127) / 128) >= 192) return p;
         // The partial sums (8 M N bytes per chunk, written and read back)
         // stay within a quarter of W's 2 K N bytes.
         if (c > K / (16 * M)) c = K / (16 * M);

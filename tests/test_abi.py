@@ -159,10 +159,14 @@ def test_workspace_sizes(lib):
     # M > 8 with fewer than 128 output tiles of 128 x 256 and K % 8 == 0: K is
     # split (chunks x tiles about 256, a multiple of 8 where within reach, at
     # least four 64-deep units per chunk) and FP32 partial sums
-    # [chunks][M][2][N rounded up to 64] follow the planes.  M=64, N=14336
-    # (56 tiles), K=4096 (64 units): 256 // 56 = 4 chunks, 224 blocks.
+    # [chunks][M][2][N rounded up to 64] follow the planes.  M=64, N=4096
+    # (16 tiles), K=4096 (64 units): 16 chunks wanted, 4096 // (16 * 64) = 4
+    # by the partial-sum bytes.
     planes = 2 * 64 * 4096 * 2
-    assert cf.cfp32_linear_workspace_bytes(64, 14336, 4096) == planes + 4 * 64 * 2 * 14336 * 4 + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 4096, 4096) == planes + 4 * 64 * 2 * 4096 * 4 + 256
+    # From 17 rows, no split where 32 x 128 tiles alone give 192 blocks or
+    # more: M=64, N=14336 (2 x 112 = 224 of them): the planes only.
+    assert cf.cfp32_linear_workspace_bytes(64, 14336, 4096) == planes + 256
     # M=40, N=520 (3 tiles), K=4104 (65 units): 85 chunks wanted, 80 for a
     # multiple of 8 blocks, 65 // 4 = 16 by length, 4104 // (16 * 40) = 6 by
     # the partial-sum bytes: 6 chunks, N rounded up to 576.

@@ -1,5 +1,6 @@
 """GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
-(fewer than 128 output tiles of 128 x 256; above 64 rows only where K
+(fewer than 128 output tiles of 128 x 256; from 17 to 64 rows only where
+32 x 128 output tiles number fewer than 192; above 64 rows only where K
 gives at least 128 blocks of four 64-deep units, 192 where the small-grid
 kernel could run the grid):
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
@@ -59,9 +60,9 @@ def check(y, A, W, what):
 
 
 # (M, K, N): the smallest M of the GEMM path, ragged N and K; many chunks;
-# the batched-decode FFN shape at the largest M that splits; a ragged last
-# unit of K; a chunk count that is not a power of two.
-SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 2048, 14336), (40, 4104, 520), (24, 2000, 777)]
+# the batched-decode FFN down projection at 64 rows; a ragged last unit of K;
+# a chunk count that is not a power of two.
+SHAPES = [(9, 1000, 777), (16, 4096, 2048), (64, 14336, 4096), (40, 4104, 520), (24, 2000, 777)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)

@@ -53,7 +53,7 @@ def without(A, W):
 PAIRS = [
     ((4096, 4096, 8192), (512, 768, 2304)),    # split + GEMM, planes of exactly 64 MiB; then no planes (split in registers)
     ((1, 4096, 14336), (3, 1000, 520)),        # small-M partial sums, twice
-    ((64, 4096, 14336), (16, 2048, 3000)),     # split K (planes + partial sums); two groups of 8 rows
+    ((64, 14336, 4096), (16, 2048, 3000)),     # split K (planes + partial sums); two groups of 8 rows
     ((8192, 4096, 14336), (333, 1000, 777)),   # planes of 128 MiB: split inside; then the generic GEMM
     ((256, 4096, 14336), (96, 4096, 14336)),   # split K above 64 rows (63 MB of planes and partial sums), twice
     ((1, 4096, 14335), (3, 1000, 777)),        # W rows not 16-byte loadable: chunked partial sums, twice

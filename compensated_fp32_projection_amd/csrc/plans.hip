@@ -56,13 +56,14 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     // 35-52 us.  Above 64 rows too the grid must stay below 128 tiles of
     // 128 x 256 (where the LDS-DMA kernel takes over), the chunks must bring
     // it to at least 128 blocks (192 where the small-grid kernel could run
-    // it instead), and the partial sums may take up to W's
-    // bytes and 56 MiB: x W at 96 / 128 / 192 / 256 x 4096 x 14336 went from
-    // 76.6 / 82.2 / 92.1 / 102.6 us (generic 32 x 128 tile) to 56.1 / 64.6 /
-    // 75.2 / 89.2 us, 128 x 8192 x 14336 from 159 to 97 us, 300 / 512 x
-    // 4096 x 4096 (144 / 128 blocks) from 62 / 80 to 48 / 63 us; where K per
-    // chunk is short (2048 x 1024 x 2048: 39 -> 55 us; 1024^3: 20 -> 33 us)
-    // it lost, which the conditions keep out.
+    // it instead), and the partial sums may take up to W's bytes and 56 MiB.
+    // Against the generic 32 x 128 tile (one launch, transposed W reads):
+    // 65 / 96 / 192 / 256 x 4096 x 14336 56.0 / 58.1 / 94-98 / 100-105 us
+    // unsplit, 48.1 / 55.1 / 74.2 / 87-90 us split; 128 x 8192 x 14336 119
+    // -> 94 us, 448 x 4096 x 5120 81 -> 64 us, 300 x 4096 x 4096 49 -> 45
+    // us; 128 x 4096 x 14336 and 512 x 4096 x 4096 are within 1-4 us either
+    // way.  Where K per chunk is short (2048 x 1024 x 2048: 39 -> 55 us;
+    // 1024^3: 20 -> 33 us) it lost, which the conditions keep out.
     constexpr int64_t kTileRows = 128, kTileCols = 256, kUnit = 64, kMinUnits = 4, kSmallRows = 64;
     constexpr int64_t kMinBlocksWide = 128, kMinBlocksKsplit = 192;
     constexpr int64_t kMaxPartBytesWide = (int64_t)56 << 20;

@@ -119,6 +119,28 @@ def test_xsplit_qkv_workload_and_layouts():
     assert_within_tolerance(y, y64, abs64, "qkv")
 
 
+@pytest.mark.parametrize("M", [33, 64])
+def test_batched_decode_rows_one_launch(M):
+    """Batched decode from 33 to 64 rows against [4096, 14336] weights: 224
+    tiles of 32 x 128 (at least 192), so K is not split and the projection is
+    one launch in either layout, with the bits of split + GEMM and of the
+    other layout, within tolerance of FP64 and below the single-FP16 error."""
+    K, N = 4096, 14336
+    assert ((M + 31) // 32) * ((N + 127) // 128) >= 192
+    A, W = workloads.random_case(M * 13 + 1, M, K, N, a_scale=20.0)
+    note(f"batched decode one launch {M}x{K}x{N}")
+    y, launches = linear(A, W)
+    assert launches in (None, 1), f"{launches} launches"
+    y_nk, launches_nk = linear(A, W, layout=cf.W_NK)
+    assert launches_nk in (None, 1), f"[N, K]: {launches_nk} launches"
+    assert np.array_equal(y.view(np.uint32), y_nk.view(np.uint32)), "[N, K] and [K, N] differ"
+    assert np.array_equal(y.view(np.uint32), two_launch(A, W).view(np.uint32)), "not the bits of split + GEMM"
+    y64, abs64 = oracle.y64(A, W)
+    assert_within_tolerance(y, y64, abs64, f"batched decode {M}x{K}x{N}")
+    _, ch, _ = oracle.linear_cf32(A[:8], W)
+    assert_better_than_single(y[:8], ch, y64[:8], abs64[:8], f"batched decode {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("M,K,N,ldx", [(512, 100, 2304, 100), (520, 1003, 2304, 1004), (600, 7, 2000, 8)])
 def test_xsplit_k_not_multiple_of_8(M, K, N, ldx):
     """K % 8 != 0 (or K < 64: only a ragged stage), rows padded to a multiple

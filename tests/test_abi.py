@@ -167,6 +167,13 @@ def test_workspace_sizes(lib):
     # From 17 rows, no split where 32 x 128 tiles alone give 192 blocks or
     # more: M=64, N=14336 (2 x 112 = 224 of them): the planes only.
     assert cf.cfp32_linear_workspace_bytes(64, 14336, 4096) == planes + 256
+    # At the edge: 33 rows x 12288 columns make exactly 2 x 96 = 192 such
+    # tiles (no split), 12160 columns 2 x 95 = 190 (split); 32 rows x 14336
+    # columns one row of 112 tiles (split).
+    planes33 = 2 * ((33 * 4096 * 2 + 255) // 256 * 256)
+    assert cf.cfp32_linear_workspace_bytes(33, 12288, 4096) == planes33 + 256
+    assert cf.cfp32_linear_workspace_bytes(33, 12160, 4096) > planes33 + 256
+    assert cf.cfp32_linear_workspace_bytes(32, 14336, 4096) > 2 * 32 * 4096 * 2 + 256
     # M=40, N=520 (3 tiles), K=4104 (65 units): 85 chunks wanted, 80 for a
     # multiple of 8 blocks, 65 // 4 = 16 by length, 4104 // (16 * 40) = 6 by
     # the partial-sum bytes: 6 chunks, N rounded up to 576.

@@ -82,12 +82,17 @@ GemmSplitPlan gemm_split_plan(int64_t M, int64_t N, int64_t K)
     const int64_t n_pad = (N + 63) / 64 * 64;
     if (M <= kSmallRows) {
         // From 17 rows, no split where the generic kernel's 32 x 128 tiles
-        // alone give 192 or more blocks: that one-launch form walks all of K
-        // without partial sums (64 / 48 x 4096 x 14336: 45.1 / 42.0 -> 40.6 /
-        // 39.2 us; [N, K] 64 rows 45.4 -> 41.6 us); on smaller grids, or
-        // with long K, split K stays ahead (64 x 4096 x 4096: 26 us either
-        // way; 64 x 14336 x 4096: 52 against 94 us).
-        if (M > 16 && ((M + 31) / 32) * ((N + 127) / 128) >= 192) return p;
+        // make 192 to 256 blocks (one per CU at most) and K <= 4096: that
+        // one-launch form walks all of K without partial sums (64 / 48 x
+        // 4096 x 14336: 45.1 / 42.0 -> 40.6 / 39.2 us; [N, K] 64 rows 45.4 ->
+        // 41.6 us; 64 x 2048 x 14336 27.5 -> 20.7 us; [N, K] 64 x 4096 x
+        // 12288 41.7 -> 39.4 us).  On smaller grids, with two blocks per CU
+        // or with longer K, split K stays ahead (64 x 4096 x 4096: 26 us
+        // either way; 64 x 14336 x 4096: 52 against 94 us; 40 / 64 x 4096 x
+        // 28672: 60.6 / 70.0 against 67.3 / 75.0 us; 64 x 8192 x 14336: 69.8
+        // against 76.3 us; GEGLU at 40 x 4096 x 2 * 14336: 67 against 91 us).
+        const int64_t tiles32 = ((M + 31) / 32) * ((N + 127) / 128);
+        if (M > 16 && tiles32 >= 192 && tiles32 <= 256 && K <= 4096) return p;
         // The partial sums (8 M N bytes per chunk, written and read back)
         // stay within a quarter of W's 2 K N bytes.
         if (c > K / (16 * M)) c = K / (16 * M);

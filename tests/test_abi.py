@@ -174,6 +174,11 @@ def test_workspace_sizes(lib):
     assert cf.cfp32_linear_workspace_bytes(33, 12288, 4096) == planes33 + 256
     assert cf.cfp32_linear_workspace_bytes(33, 12160, 4096) > planes33 + 256
     assert cf.cfp32_linear_workspace_bytes(32, 14336, 4096) > 2 * 32 * 4096 * 2 + 256
+    # Above 256 such tiles (40 x 28672: 448), or K above 4096, K is split.
+    assert cf.cfp32_linear_workspace_bytes(40, 28672, 4096) > 2 * 40 * 4096 * 2 + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 16384, 4096) == planes + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 16512, 4096) > planes + 256
+    assert cf.cfp32_linear_workspace_bytes(64, 14336, 4104) > 2 * 64 * 4104 * 2 + 256
     # M=40, N=520 (3 tiles), K=4104 (65 units): 85 chunks wanted, 80 for a
     # multiple of 8 blocks, 65 // 4 = 16 by length, 4104 // (16 * 40) = 6 by
     # the partial-sum bytes: 6 chunks, N rounded up to 576.

@@ -1,6 +1,6 @@
 """GPU tests of the batched-decode paths of cfp32_linear / cfp32_linear_ex
-(fewer than 128 output tiles of 128 x 256; from 17 to 64 rows only where
-32 x 128 output tiles number fewer than 192; above 64 rows only where K
+(fewer than 128 output tiles of 128 x 256; from 17 to 64 rows except where
+32 x 128 output tiles number 192 to 256 and K <= 4096; above 64 rows only where K
 gives at least 128 blocks of four 64-deep units, 192 where the small-grid
 kernel could run the grid):
   * split K (the GEMM path; K % 8 == 0): K is cut into chunks of 64-deep
